@@ -1,0 +1,74 @@
+// Device helpers shared by the gfx950 kernels of the Shampoo library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/shampoo.h"
+
+namespace shp {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
+
+// Workgroups are handed to the XCDs round-robin (id % 8).  This maps the
+// hardware id to a logical id so that each XCD receives one contiguous range
+// of logical tiles: the tiles of a factor then share one L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t hw, uint32_t total) {
+  const uint32_t q = total / kXcds, r = total % kXcds;
+  const uint32_t xcd = hw % kXcds, local = hw / kXcds;
+  return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// Deterministic sum over a workgroup of `nthreads` threads (fixed tree order).
+// `red` must hold nthreads / 64 floats.  Returns the total in every thread.
+template <int kThreads>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x % kWave) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bool degenerate(int32_t st) {
+  return (st & (SHAMPOO_BLK_ZERO | SHAMPOO_BLK_NONPOS_RQ)) != 0;
+}
+
+// Scale constant as used by the iterations: a degenerate factor keeps c = 1
+// so that its (discarded) iterates stay finite.
+__device__ __forceinline__ float safe_c(const shampoo_scale* sc, const int32_t* status, int64_t f) {
+  const float c = sc[f].c;
+  if (status != nullptr && degenerate(status[f])) return 1.f;
+  return c;
+}
+
+}  // namespace shp

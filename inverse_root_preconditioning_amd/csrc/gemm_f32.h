@@ -1,0 +1,457 @@
+// Batched fp32 MFMA matrix product for gfx950 with fused epilogues.
+//
+// One launch computes C_i = A_i * B_i for every item i of up to two jobs (the
+// Newton-DB update Y E and E Z, for instance, run as two jobs of one launch).
+// Each workgroup of 256 threads (4 waves, 2 x 2) owns one (64 TM) x (64 TN)
+// output tile of one item; each wave owns (32 TM) x (32 TN) of it as TM x TN
+// blocks of V_MFMA_F32_32X32X2_F32.  Operand tiles of 32 k-values are staged
+// through LDS (double-buffered, one barrier per stage) from either a dense
+// stack of B x B row-major matrices or a table of block descriptors (zero
+// outside the block).  The epilogue turns the fp32 accumulators into the
+// output of the step (E = (3I - P)/2, an EMA, a Clenshaw term, ...) so that
+// no separate elementwise pass over HBM is needed.
+//
+// k-order within a group of 8: for MFMA j (0..3) lane (r, h) supplies
+// element k = 8 g + 4 h + j of its row of A and column of B, so every lane
+// reads 4 consecutive k values at once; the sum over j and h covers all 8.
+#pragma once
+
+#include "common.h"
+
+namespace shp {
+
+enum { KCONTIG = 0, MNCONTIG = 1 };
+
+constexpr int kGemmThreads = 256;
+constexpr int kBK = 32;
+
+// One operand of a job: a dense stack (desc == nullptr) or descriptors.
+struct Operand {
+  const float* base;
+  const shampoo_block* desc;
+};
+
+// Storage view of one item of an operand.
+struct OperandView {
+  const float* p;
+  int64_t ld;
+  int rows, cols;  // valid storage extent
+  bool vec;        // 16-byte vector loads allowed
+};
+
+__device__ __forceinline__ OperandView operand_view(const Operand& op, int64_t item, int B) {
+  OperandView v;
+  if (op.desc == nullptr) {
+    v.p = op.base + item * (int64_t)B * B;
+    v.ld = B;
+    v.rows = B;
+    v.cols = B;
+    v.vec = true;
+  } else {
+    const shampoo_block d = op.desc[item];
+    const bool ok = d.ptr != nullptr && d.rows >= 0 && d.cols >= 0 && d.rows <= B && d.cols <= B &&
+                    d.ld >= d.cols;
+    v.p = d.ptr;
+    v.ld = d.ld;
+    v.rows = ok ? d.rows : 0;
+    v.cols = ok ? d.cols : 0;
+    v.vec = ((reinterpret_cast<uintptr_t>(d.ptr) & 15u) == 0) && ((d.ld & 3) == 0);
+  }
+  return v;
+}
+
+// Tile staging for one operand: MN x 32 values (MN rows of the product).
+template <int MN, int LAYOUT, bool DESC>
+struct Stager {
+  static constexpr int kLoads = MN / 32;  // float4 per thread per stage
+  static constexpr int kStride = (LAYOUT == KCONTIG) ? (kBK + 4) : (MN + 4);
+  static constexpr int kFloats = (LAYOUT == KCONTIG) ? MN * (kBK + 4) : kBK * (MN + 4);
+  floatx4 r[kLoads];
+
+  __device__ __forceinline__ void load(const OperandView& v, int mn0, int k0) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      const int idx = tid + kGemmThreads * it;
+      int srow, scol;
+      if (LAYOUT == KCONTIG) {
+        srow = mn0 + (idx >> 3);
+        scol = k0 + (idx & 7) * 4;
+      } else {
+        srow = k0 + idx / (MN / 4);
+        scol = mn0 + (idx % (MN / 4)) * 4;
+      }
+      if (!DESC) {
+        r[it] = *reinterpret_cast<const floatx4*>(v.p + (int64_t)srow * v.ld + scol);
+      } else {
+        floatx4 x = {0.f, 0.f, 0.f, 0.f};
+        if (srow < v.rows) {
+          const float* src = v.p + (int64_t)srow * v.ld + scol;
+          if (v.vec && scol + 3 < v.cols) {
+            x = *reinterpret_cast<const floatx4*>(src);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (scol + e < v.cols) x[e] = src[e];
+          }
+        }
+        r[it] = x;
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(float* lds) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < kLoads; ++it) {
+      const int idx = tid + kGemmThreads * it;
+      int off;
+      if (LAYOUT == KCONTIG)
+        off = (idx >> 3) * kStride + (idx & 7) * 4;
+      else
+        off = (idx / (MN / 4)) * kStride + (idx % (MN / 4)) * 4;
+      *reinterpret_cast<floatx4*>(lds + off) = r[it];
+    }
+  }
+
+  // Fragment of 4 consecutive k (8 g + 4 h + j, j = 0..3) at row mb + r.
+  __device__ __forceinline__ static floatx4 frag(const float* lds, int mb, int g, int lane) {
+    const int rr = lane & 31, h = lane >> 5;
+    if (LAYOUT == KCONTIG) {
+      return *reinterpret_cast<const floatx4*>(lds + (mb + rr) * kStride + g * 8 + h * 4);
+    } else {
+      floatx4 x;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = lds[(g * 8 + h * 4 + j) * kStride + mb + rr];
+      return x;
+    }
+  }
+};
+
+// Launch parameters; Epi::Job carries the epilogue's per-job arguments.
+template <class Epi>
+struct GemmLaunch {
+  Operand a[2];
+  Operand b[2];
+  typename Epi::Job e[2];
+  int64_t nitems;      // items per job
+  int B;
+  int tiles_n;         // B / BN
+  int tiles_per_item;  // tiles_m * tiles_n, or T (T + 1) / 2 when sym
+  int sym;             // product is symmetric: upper tiles only, mirrored stores
+  uint32_t total;      // njobs * nitems * tiles_per_item
+};
+
+template <int TM, int TN, int LA, int LB, bool DA, bool DB, class Epi>
+__global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLaunch<Epi> P) {
+  constexpr int BM = 64 * TM, BN = 64 * TN;
+  using SA = Stager<BM, LA, DA>;
+  using SB = Stager<BN, LB, DB>;
+  __shared__ __attribute__((aligned(16))) float lds[2 * (SA::kFloats + SB::kFloats)];
+  __shared__ float red[kGemmThreads / kWave];
+
+  const uint32_t lid = xcd_remap(blockIdx.x, P.total);
+  const uint32_t per_job = (uint32_t)P.nitems * P.tiles_per_item;
+  const int job = lid / per_job;
+  const uint32_t rem = lid - job * per_job;
+  const int64_t item = rem / P.tiles_per_item;
+  int t = rem - (uint32_t)item * P.tiles_per_item;
+  int tm, tn;
+  if (!P.sym) {
+    tm = t / P.tiles_n;
+    tn = t - tm * P.tiles_n;
+  } else {  // upper-triangular tile enumeration, row by row
+    tm = 0;
+    int rowlen = P.tiles_n;
+    while (t >= rowlen) {
+      t -= rowlen;
+      ++tm;
+      --rowlen;
+    }
+    tn = tm + t;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const OperandView va = operand_view(P.a[job], item, P.B);
+  const OperandView vb = operand_view(P.b[job], item, P.B);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = (wave >> 1) * 32 * TM;  // wave's row offset inside the tile
+  const int wn = (wave & 1) * 32 * TN;
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  SA sa;
+  SB sb;
+  constexpr int kStage = SA::kFloats + SB::kFloats;
+
+  const int nstages = P.B / kBK;
+  sa.load(va, m0, 0);
+  sb.load(vb, n0, 0);
+  sa.store(lds);
+  sb.store(lds + SA::kFloats);
+  __syncthreads();
+
+  for (int s = 0; s < nstages; ++s) {
+    const int cur = s & 1;
+    const float* bufA = lds + cur * kStage;
+    const float* bufB = bufA + SA::kFloats;
+    if (s + 1 < nstages) {
+      sa.load(va, m0, (s + 1) * kBK);
+      sb.load(vb, n0, (s + 1) * kBK);
+    }
+#pragma unroll
+    for (int g = 0; g < kBK / 8; ++g) {
+      floatx4 fa[TM], fb[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[i] = SA::frag(bufA, wm + 32 * i, g, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[j] = SB::frag(bufB, wn + 32 * j, g, lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][q], fb[j][q], acc[i][j], 0, 0, 0);
+    }
+    if (s + 1 < nstages) {
+      float* nxt = lds + (cur ^ 1) * kStage;
+      sa.store(nxt);
+      sb.store(nxt + SA::kFloats);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue.  Accumulator e of block (i, j) sits at
+  // row = 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = 32 j + lane % 32.
+  typename Epi::Tile tile(P.e[job], item, P.B);
+  const bool diag_tile = P.sym && tm == tn;
+  const bool mirror = P.sym && tm != tn;
+  float part = 0.f;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int col = n0 + wn + 32 * j + (lane & 31);
+        const float v = acc[i][j][e];
+        if (diag_tile) {
+          if (row <= col) {
+            part += tile.store(row, col, v);
+            if (row != col) tile.store(col, row, v);
+          }
+        } else {
+          part += tile.store(row, col, v);
+          if (mirror) tile.store(col, row, v);
+        }
+      }
+  if (Epi::kReduce) {
+    const float tot = block_sum<kGemmThreads>(part, red);
+    if (threadIdx.x == 0) tile.partial(tm * P.tiles_n + tn, tot);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Epilogues.  Tile(job, item, B) is built once per workgroup; store(row, col,
+// v) writes the output for one accumulator and returns its contribution to
+// the tile's reduction (if any); partial(t, sum) stores that reduction.
+// ---------------------------------------------------------------------------
+
+// out = mult * acc + beta * cin (cin may alias out); X = I for a degenerate
+// factor when `status` is given.  mult = alpha * extra * c_f^pexp when
+// `scale` is given, else alpha.
+struct EpiStore {
+  static constexpr bool kReduce = false;
+  struct Job {
+    float* out;
+    const float* cin;
+    float alpha, beta;
+    const shampoo_scale* scale;
+    const int32_t* status;
+    float pexp, extra;
+  };
+  struct Tile {
+    float* out;
+    const float* cin;
+    float mult, beta;
+    bool ident;
+    int B;
+    __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
+      const int64_t off = item * (int64_t)B_ * B_;
+      out = j.out + off;
+      cin = j.cin ? j.cin + off : nullptr;
+      beta = j.beta;
+      mult = j.alpha;
+      if (j.scale) mult *= j.extra * powf(safe_c(j.scale, j.status, item), j.pexp);
+      ident = j.status && degenerate(j.status[item]);
+    }
+    __device__ __forceinline__ float store(int row, int col, float v) {
+      const int64_t idx = (int64_t)row * B + col;
+      float o = mult * v;
+      if (cin) o += beta * cin[idx];
+      if (ident) o = (row == col) ? 1.f : 0.f;
+      out[idx] = o;
+      return 0.f;
+    }
+    __device__ void partial(int, float) {}
+  };
+};
+
+// Output through a block descriptor: only rows x cols of the block is written.
+struct EpiStoreDesc {
+  static constexpr bool kReduce = false;
+  struct Job {
+    const shampoo_block* out;
+  };
+  struct Tile {
+    float* p;
+    int64_t ld;
+    int rows, cols;
+    __device__ Tile(const Job& j, int64_t item, int B) {
+      const shampoo_block d = j.out[item];
+      const bool ok = d.ptr != nullptr && d.rows >= 0 && d.cols >= 0 && d.rows <= B && d.cols <= B &&
+                      d.ld >= d.cols;
+      p = d.ptr;
+      ld = d.ld;
+      rows = ok ? d.rows : 0;
+      cols = ok ? d.cols : 0;
+    }
+    __device__ __forceinline__ float store(int row, int col, float v) {
+      if (row < rows && col < cols) p[(int64_t)row * ld + col] = v;
+      return 0.f;
+    }
+    __device__ void partial(int, float) {}
+  };
+};
+
+// Newton-DB: P = Z Y -> E = (3 I - P) / 2, reduction ||I - P||_F^2.
+struct EpiNdbE {
+  static constexpr bool kReduce = true;
+  struct Job {
+    float* e;
+    float* partials;  // [nitems][tiles]
+    int tiles;
+  };
+  struct Tile {
+    float* e;
+    float* part;
+    int B;
+    __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
+      e = j.e + item * (int64_t)B_ * B_;
+      part = j.partials + item * j.tiles;
+    }
+    __device__ __forceinline__ float store(int row, int col, float v) {
+      const float d = (row == col) ? 1.f : 0.f;
+      e[(int64_t)row * B + col] = 1.5f * d - 0.5f * v;
+      const float r = d - v;
+      return r * r;
+    }
+    __device__ void partial(int t, float s) { part[t] = s; }
+  };
+};
+
+// Coupled Newton: M' = C^p M -> store M' and C' = ((p+1) I - M') / p,
+// reduction ||I - M'||_F^2.
+struct EpiCnM {
+  static constexpr bool kReduce = true;
+  struct Job {
+    float* m;
+    float* c;
+    float* partials;
+    int tiles;
+    float p;
+  };
+  struct Tile {
+    float* m;
+    float* c;
+    float* part;
+    float p1, pinv;
+    int B;
+    __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
+      const int64_t off = item * (int64_t)B_ * B_;
+      m = j.m + off;
+      c = j.c + off;
+      part = j.partials + item * j.tiles;
+      p1 = j.p + 1.f;
+      pinv = 1.f / j.p;
+    }
+    __device__ __forceinline__ float store(int row, int col, float v) {
+      const int64_t idx = (int64_t)row * B + col;
+      const float d = (row == col) ? 1.f : 0.f;
+      m[idx] = v;
+      c[idx] = (p1 * d - v) * pinv;
+      const float r = d - v;
+      return r * r;
+    }
+    __device__ void partial(int t, float s) { part[t] = s; }
+  };
+};
+
+// Clenshaw step with T = 2 A_s - I applied in the epilogue (acc = A_s b1):
+//   b = cj I + 4 acc - 2 b1 - b2                        (final == 0)
+//   X = mult (cj I + 2 acc - b1 - b2), I if degenerate   (final == 1, cj = c_0)
+// An optional bf16 copy of b is written for the next bf16 product.
+struct EpiClenshaw {
+  static constexpr bool kReduce = false;
+  struct Job {
+    float* out;
+    uint16_t* out_bf16;
+    const float* b1;
+    const float* b2;
+    float cj;
+    int final;
+    const shampoo_scale* scale;
+    const int32_t* status;
+    float pexp;
+  };
+  struct Tile {
+    float* out;
+    uint16_t* obf;
+    const float* b1;
+    const float* b2;
+    float cj, mult, k1, k2;
+    bool ident;
+    int B;
+    __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
+      const int64_t off = item * (int64_t)B_ * B_;
+      out = j.out + off;
+      obf = j.out_bf16 ? j.out_bf16 + off : nullptr;
+      b1 = j.b1 + off;
+      b2 = j.b2 + off;
+      cj = j.cj;
+      if (j.final) {
+        k1 = 2.f;
+        k2 = 1.f;
+        mult = powf(safe_c(j.scale, j.status, item), j.pexp);
+        ident = j.status && degenerate(j.status[item]);
+      } else {
+        k1 = 4.f;
+        k2 = 2.f;
+        mult = 1.f;
+        ident = false;
+      }
+    }
+    __device__ __forceinline__ float store(int row, int col, float v) {
+      const int64_t idx = (int64_t)row * B + col;
+      const float d = (row == col) ? cj : 0.f;
+      float o = mult * (d + k1 * v - k2 * b1[idx] - b2[idx]);
+      if (ident) o = (row == col) ? 1.f : 0.f;
+      out[idx] = o;
+      if (obf) obf[idx] = f32_to_bf16_bits(o);
+      return 0.f;
+    }
+    __device__ void partial(int, float) {}
+  };
+};
+
+}  // namespace shp

@@ -1,0 +1,379 @@
+// Reductions, power-iteration panel steps and elementwise prologues.
+#pragma once
+
+#include "gemm_f32.h"
+
+namespace shp {
+
+// ---------------------------------------------------------------------------
+// Trace and damping: sc[f].trace = tr(F_f), sc[f].eps = eps_rel tr / B.
+// One workgroup per factor, fixed-order sum.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) trace_kernel(const float* __restrict__ F, int B, float eps_rel,
+                                                    shampoo_scale* __restrict__ sc) {
+  __shared__ float red[4];
+  const int64_t f = blockIdx.x;
+  const float* A = F + f * (int64_t)B * B;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < B; i += 256) s += A[(int64_t)i * B + i];
+  const float t = block_sum<256>(s, red);
+  if (threadIdx.x == 0) {
+    sc[f].trace = t;
+    sc[f].eps = eps_rel * t / (float)B;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Frobenius norm: sum of squares in `chunks` slices per factor, then one wave
+// per factor finishes ||F + eps I||_F^2 = sum F^2 + 2 eps tr + B eps^2.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) sumsq_kernel(const float* __restrict__ F, int64_t per_factor,
+                                                    int chunks, float* __restrict__ partials) {
+  __shared__ float red[4];
+  const int64_t f = blockIdx.x / chunks;
+  const int chunk = blockIdx.x - (int)(f * chunks);
+  const int64_t n4 = per_factor / 4;
+  const int64_t len = (n4 + chunks - 1) / chunks;
+  const int64_t lo = chunk * len, hi = min(n4, lo + len);
+  const floatx4* p = reinterpret_cast<const floatx4*>(F + f * per_factor);
+  float s = 0.f;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
+    const floatx4 v = p[i];
+    s += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  }
+  const float t = block_sum<256>(s, red);
+  if (threadIdx.x == 0) partials[f * chunks + chunk] = t;
+}
+
+__device__ __forceinline__ int32_t scale_status(float trace, float lam) {
+  int32_t st = 0;
+  if (!isfinite(trace)) {
+    st |= SHAMPOO_BLK_NONFINITE;
+  } else if (trace == 0.f) {
+    st |= SHAMPOO_BLK_ZERO;
+  }
+  if (!isfinite(lam)) {
+    st |= SHAMPOO_BLK_NONFINITE;
+  } else if (lam <= 0.f && !(st & SHAMPOO_BLK_ZERO)) {
+    st |= SHAMPOO_BLK_NONPOS_RQ;
+  }
+  return st;
+}
+
+// One wave per factor.
+__global__ void __launch_bounds__(64) frob_finalize_kernel(const float* __restrict__ partials, int chunks,
+                                                          int B, shampoo_scale* __restrict__ sc,
+                                                          int32_t* __restrict__ status) {
+  const int64_t f = blockIdx.x;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < chunks; i += 64) s += partials[f * chunks + i];
+  s = wave_sum(s);
+  if (threadIdx.x == 0) {
+    const float tr = sc[f].trace, eps = sc[f].eps;
+    const float n2 = s + 2.f * eps * tr + (float)B * eps * eps;
+    const float lam = sqrtf(n2);
+    sc[f].lambda = lam;
+    sc[f].c = lam;
+    status[f] = scale_status(tr, lam);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Power iteration.  Each step computes W = (F + eps I) V diag(s) for one
+// PANEL-row panel of one factor on MFMA (32 x 32 blocks, K = B), where
+// s_j = 1 / ||previous W column j|| (1 on the first step), and writes
+// per-panel column sums of W^2 (next step's norms) and, on the last step,
+// of v~_j w_j with v~ = V diag(s) (the Rayleigh quotients).  With a 128-row
+// panel each of the 4 waves owns one 32-row block; with a 64-row panel two
+// waves share a block and split the k-groups, summed through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kPiCols = 32;
+
+struct PiArgs {
+  const float* F;
+  const float* vin;        // [nf][B][ldv]
+  int ldv;                 // r for the caller's start vectors, 32 for W buffers
+  int r;                   // valid columns
+  float* wout;             // [nf][B][32] (unused on the last step)
+  const float* norm_in;    // [nf][npanels][32] or null on the first step
+  float* norm_out;         // [nf][npanels][32]
+  float* rq_out;           // [nf][npanels][32], last step only
+  const shampoo_scale* sc; // eps
+  int B;
+  int npanels;
+  uint32_t total;          // nf * npanels
+  int last;
+};
+
+template <int PANEL>
+__global__ void __launch_bounds__(256, 2) pi_step_kernel(const PiArgs P) {
+  constexpr int RB = PANEL / 32;  // row blocks per panel
+  constexpr int KS = 4 / RB;      // waves sharing a row block (k split)
+  using SA = Stager<PANEL, KCONTIG, false>;
+  using SV = Stager<kPiCols, MNCONTIG, true>;
+  __shared__ __attribute__((aligned(16))) float lds[2 * (SA::kFloats + SV::kFloats)];
+  __shared__ float s_col[kPiCols];
+  __shared__ float colsum[2][RB][kPiCols];
+
+  const uint32_t lid = xcd_remap(blockIdx.x, P.total);
+  const int64_t f = lid / P.npanels;
+  const int panel = lid - (uint32_t)f * P.npanels;
+  const int m0 = panel * PANEL;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rb = wave % RB, ks = wave / RB;
+
+  if (threadIdx.x < kPiCols) {
+    const int j = threadIdx.x;
+    float s = 0.f;
+    if (j < P.r) {
+      if (P.norm_in == nullptr) {
+        s = 1.f;
+      } else {
+        float n2 = 0.f;
+        for (int p = 0; p < P.npanels; ++p) n2 += P.norm_in[(f * P.npanels + p) * kPiCols + j];
+        s = (n2 > 0.f) ? 1.f / sqrtf(n2) : ((n2 == 0.f) ? 0.f : n2);  // NaN propagates
+      }
+    }
+    s_col[j] = s;
+  }
+
+  OperandView va;
+  va.p = P.F + f * (int64_t)P.B * P.B;
+  va.ld = P.B;
+  va.rows = P.B;
+  va.cols = P.B;
+  va.vec = true;
+  OperandView vv;
+  vv.p = P.vin + f * (int64_t)P.B * P.ldv;
+  vv.ld = P.ldv;
+  vv.rows = P.B;
+  vv.cols = P.r;
+  vv.vec = (P.ldv & 3) == 0;
+
+  floatx16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+
+  SA sa;
+  SV sv;
+  const int stage = SA::kFloats + SV::kFloats;
+  const int nstages = P.B / kBK;
+  sa.load(va, m0, 0);
+  sv.load(vv, 0, 0);
+  sa.store(lds);
+  sv.store(lds + SA::kFloats);
+  __syncthreads();
+  for (int s = 0; s < nstages; ++s) {
+    const int cur = s & 1;
+    float* bufA = lds + cur * stage;
+    float* bufV = bufA + SA::kFloats;
+    if (s + 1 < nstages) {
+      sa.load(va, m0, (s + 1) * kBK);
+      sv.load(vv, 0, (s + 1) * kBK);
+    }
+#pragma unroll
+    for (int gg = 0; gg < kBK / 8 / KS; ++gg) {
+      const int g = gg * KS + ks;
+      const floatx4 fa = SA::frag(bufA, rb * 32, g, lane);
+      const floatx4 fv = SV::frag(bufV, 0, g, lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[q], fv[q], acc, 0, 0, 0);
+    }
+    if (s + 1 < nstages) {
+      float* nA = lds + (cur ^ 1) * stage;
+      sa.store(nA);
+      sv.store(nA + SA::kFloats);
+    }
+    __syncthreads();
+  }
+
+  if (KS > 1) {  // waves with ks > 0 hand their partial sums to ks == 0 (lds is free now)
+    if (ks == 1) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lds[(rb * 16 + e) * 64 + lane] = acc[e];
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += lds[(rb * 16 + e) * 64 + lane];
+    }
+  }
+
+  const int j = lane & 31;
+  if (ks == 0) {
+    const float sj = s_col[j];
+    const float eps = P.sc[f].eps;
+    float nsum = 0.f, rsum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = m0 + rb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      const float v = (j < P.r) ? vv.p[(int64_t)row * P.ldv + j] * sj : 0.f;
+      const float w = acc[e] * sj + eps * v;
+      if (!P.last) P.wout[(f * P.B + row) * kPiCols + j] = w;
+      nsum += w * w;
+      rsum += v * w;
+    }
+    nsum += __shfl_xor(nsum, 32, kWave);
+    rsum += __shfl_xor(rsum, 32, kWave);
+    if (lane < 32) {
+      colsum[0][rb][j] = nsum;
+      colsum[1][rb][j] = rsum;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kPiCols) {
+    const int c = threadIdx.x;
+    const int64_t o = (f * P.npanels + panel) * kPiCols + c;
+    float n = 0.f, q = 0.f;
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      n += colsum[0][b][c];
+      q += colsum[1][b][c];
+    }
+    P.norm_out[o] = n;
+    if (P.last) P.rq_out[o] = q;
+  }
+}
+
+// One wave per factor: lambda = max_j q_j, c = safety lambda, status bits.
+__global__ void __launch_bounds__(64) pi_finalize_kernel(const float* __restrict__ rq, int npanels, int r,
+                                                        float safety, shampoo_scale* __restrict__ sc,
+                                                        int32_t* __restrict__ status) {
+  const int64_t f = blockIdx.x;
+  const int j = threadIdx.x;
+  float q = -INFINITY;
+  int nan = 0;
+  if (j < r) {
+    q = 0.f;
+    for (int p = 0; p < npanels; ++p) q += rq[(f * npanels + p) * kPiCols + j];
+    nan = (q != q);
+  }
+  const float lam0 = wave_max(nan ? -INFINITY : q);
+  const int any_nan = __any(nan);
+  if (j == 0) {
+    const float lam = any_nan ? __int_as_float(0x7fc00000) : lam0;
+    const float tr = sc[f].trace;
+    sc[f].lambda = lam;
+    sc[f].c = safety * lam;
+    status[f] = scale_status(tr, lam);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Elementwise passes over whole B x B items (float4 per thread).  Each
+// workgroup covers `per_block` float4 of one item and writes one partial of
+// the residual sum for it.
+// ---------------------------------------------------------------------------
+enum {
+  EW_NDB_START = 0,   // y = a x + b I (optional store), e = (3 I - y) / 2, sum (I - y)^2
+  EW_CN_START = 1,    // m = a x + b I, c = ((p+1) I - m) / p, sum (I - m)^2
+  EW_CHEBY_START = 2, // as = a x + b I, bd = cd I, bd1 = cd1 I + 2 cd (2 as - I)
+  EW_SCALE_COPY = 3,  // out = mult x (mult = extra c^pexp), I if degenerate
+  EW_CHEBY_LINEAR = 4 // out = mult (c0 I + c1 (2 (a x + b I) - I)), I if degenerate
+};
+
+struct EwArgs {
+  const float* x;              // input stack
+  float* out0;                 // y | m | as | out
+  float* out1;                 // e | c | bd
+  float* out2;                 //     |    | bd1
+  float* partials;             // [nf][chunks] or null
+  const shampoo_scale* sc;     // per-factor c and eps (null: a = ua, b = ub)
+  const int32_t* status;
+  float ua, ub;                // uniform a, b when sc == null
+  float p;                     // root order
+  float c0, c1;                // Chebyshev coefficients (c_d, c_{d-1} or c_0, c_1)
+  float pexp, extra;           // scale copy: mult = extra c^pexp
+  int B;
+  int chunks;                  // workgroups per item
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(256) ew_kernel(const EwArgs P) {
+  __shared__ float red[4];
+  const int64_t f = blockIdx.x / P.chunks;
+  const int chunk = blockIdx.x - (int)(f * P.chunks);
+  const int64_t n = (int64_t)P.B * P.B;
+  const int64_t n4 = n / 4;
+  const int64_t len = (n4 + P.chunks - 1) / P.chunks;
+  const int64_t lo = chunk * len, hi = min(n4, lo + len);
+  const int64_t off = f * n;
+
+  float a = P.ua, b = P.ub, mult = 1.f;
+  bool ident = false;
+  if (P.sc != nullptr) {
+    const float c = safe_c(P.sc, P.status, f);
+    if (MODE == EW_SCALE_COPY || MODE == EW_CHEBY_LINEAR) {
+      mult = P.extra * powf(c, P.pexp);
+      if (MODE == EW_CHEBY_LINEAR) {
+        a = 1.f / c;
+        b = P.sc[f].eps / c;
+      }
+    } else {
+      a = 1.f / c;
+      b = P.sc[f].eps / c;
+    }
+    if (P.status != nullptr && degenerate(P.status[f])) {
+      ident = true;
+      if (MODE != EW_SCALE_COPY && MODE != EW_CHEBY_LINEAR) {
+        a = 0.f;
+        b = 0.f;
+      }
+    }
+  }
+  const float pinv = 1.f / P.p, p1 = P.p + 1.f;
+  float part = 0.f;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
+    const floatx4 xv = *reinterpret_cast<const floatx4*>(P.x + off + 4 * i);
+    floatx4 o0, o1, o2;
+    const int row = (int)((4 * i) / P.B);
+    const int col0 = (int)(4 * i - (int64_t)row * P.B);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = (row == col0 + e) ? 1.f : 0.f;
+      const float y = a * xv[e] + b * d;
+      if (MODE == EW_NDB_START) {
+        o0[e] = y;
+        o1[e] = 1.5f * d - 0.5f * y;
+        part += (d - y) * (d - y);
+      } else if (MODE == EW_CN_START) {
+        o0[e] = y;
+        o1[e] = (p1 * d - y) * pinv;
+        part += (d - y) * (d - y);
+      } else if (MODE == EW_CHEBY_START) {
+        o0[e] = y;
+        o1[e] = P.c0 * d;
+        o2[e] = P.c1 * d + 2.f * P.c0 * (2.f * y - d);
+      } else if (MODE == EW_SCALE_COPY) {
+        o0[e] = ident ? d : mult * xv[e];
+      } else {
+        o0[e] = ident ? d : mult * (P.c0 * d + P.c1 * (2.f * y - d));
+      }
+    }
+    if (P.out0) *reinterpret_cast<floatx4*>(P.out0 + off + 4 * i) = o0;
+    if (MODE == EW_NDB_START || MODE == EW_CN_START || MODE == EW_CHEBY_START)
+      *reinterpret_cast<floatx4*>(P.out1 + off + 4 * i) = o1;
+    if (MODE == EW_CHEBY_START) *reinterpret_cast<floatx4*>(P.out2 + off + 4 * i) = o2;
+  }
+  if (P.partials != nullptr) {
+    const float t = block_sum<256>(part, red);
+    if (threadIdx.x == 0) P.partials[f * P.chunks + chunk] = t;
+  }
+}
+
+// resid[f][col] = sqrt(sum of partials[f][:count]); NONFINITE if not finite.
+__global__ void __launch_bounds__(64) resid_kernel(const float* __restrict__ partials, int count,
+                                                  float* __restrict__ resid, int ncols, int col,
+                                                  int32_t* __restrict__ status) {
+  const int64_t f = blockIdx.x;
+  float s = 0.f;
+  for (int i = threadIdx.x; i < count; i += 64) s += partials[f * count + i];
+  s = wave_sum(s);
+  if (threadIdx.x == 0) {
+    const float r = sqrtf(s);
+    if (resid != nullptr) resid[f * ncols + col] = r;
+    if (!isfinite(r) && status != nullptr && !degenerate(status[f])) status[f] |= SHAMPOO_BLK_NONFINITE;
+  }
+}
+
+}  // namespace shp

@@ -1,0 +1,867 @@
+// C entry points of the Shampoo block-preconditioner library (gfx950).
+//
+// Every call validates its arguments on the host, carves its scratch buffers
+// out of the caller's workspace and enqueues kernels on the caller's stream;
+// nothing is allocated and nothing synchronises.
+#include <cmath>
+#include <cstring>
+
+#include "gemm_bf16.h"
+#include "kernels_misc.h"
+
+using namespace shp;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxB = 16384;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_B(int B) { return B >= 64 && B <= kMaxB && (B % 64) == 0; }
+
+int tile_of(int B) { return (B % 128 == 0) ? 128 : 64; }
+
+int check_launch() { return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMPOO_EHIP; }
+
+// Sequential carving of a workspace; `base == nullptr` only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+size_t stack_elems(int64_t n, int B) { return (size_t)n * (size_t)B * (size_t)B; }
+
+int ew_chunks(int B) {
+  const int64_t n4 = (int64_t)B * B / 4;
+  int64_t c = n4 / 4096;
+  if (c < 1) c = 1;
+  if (c > 64) c = 64;
+  return (int)c;
+}
+
+int gemm_tiles(int B) {
+  const int t = B / tile_of(B);
+  return t * t;
+}
+
+// ---------------------------------------------------------------------------
+// Batched product launch.
+// ---------------------------------------------------------------------------
+template <int LA, int LB, bool DA, bool DB, class Epi>
+int run_gemm(const Operand* a, const Operand* b, const typename Epi::Job* e, int njobs, int64_t nitems,
+             int B, bool sym, hipStream_t st) {
+  GemmLaunch<Epi> P;
+  memset(&P, 0, sizeof(P));
+  for (int j = 0; j < njobs; ++j) {
+    P.a[j] = a[j];
+    P.b[j] = b[j];
+    P.e[j] = e[j];
+  }
+  const int T = tile_of(B);
+  P.nitems = nitems;
+  P.B = B;
+  P.tiles_n = B / T;
+  P.tiles_per_item = sym ? P.tiles_n * (P.tiles_n + 1) / 2 : P.tiles_n * P.tiles_n;
+  P.sym = sym ? 1 : 0;
+  const uint64_t total = (uint64_t)njobs * (uint64_t)nitems * (uint64_t)P.tiles_per_item;
+  if (total == 0) return SHAMPOO_OK;
+  if (total > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
+  P.total = (uint32_t)total;
+  if (T == 128)
+    hipLaunchKernelGGL((gemm_f32_kernel<2, 2, LA, LB, DA, DB, Epi>), dim3(P.total), dim3(kGemmThreads), 0, st, P);
+  else
+    hipLaunchKernelGGL((gemm_f32_kernel<1, 1, LA, LB, DA, DB, Epi>), dim3(P.total), dim3(kGemmThreads), 0, st, P);
+  return check_launch();
+}
+
+Operand dense(const float* p) { return Operand{p, nullptr}; }
+Operand blocks(const shampoo_block* d) { return Operand{nullptr, d}; }
+
+// Plain product of two dense stacks, C = A B, with the given epilogue.
+template <class Epi>
+int gemm_nn(const float* const* A, const float* const* Bm, const typename Epi::Job* e, int njobs, int64_t n,
+            int B, hipStream_t st) {
+  Operand oa[2], ob[2];
+  for (int j = 0; j < njobs; ++j) {
+    oa[j] = dense(A[j]);
+    ob[j] = dense(Bm[j]);
+  }
+  return run_gemm<KCONTIG, MNCONTIG, false, false, Epi>(oa, ob, e, njobs, n, B, false, st);
+}
+
+template <int MODE>
+int run_ew(const EwArgs& a, int64_t nf, hipStream_t st) {
+  const uint64_t grid = (uint64_t)nf * a.chunks;
+  if (grid == 0) return SHAMPOO_OK;
+  if (grid > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
+  hipLaunchKernelGGL(ew_kernel<MODE>, dim3((uint32_t)grid), dim3(256), 0, st, a);
+  return check_launch();
+}
+
+int run_resid(const float* partials, int count, float* resid, int ncols, int col, int32_t* status, int64_t nf,
+              hipStream_t st) {
+  hipLaunchKernelGGL(resid_kernel, dim3((uint32_t)nf), dim3(64), 0, st, partials, count, resid, ncols, col, status);
+  return check_launch();
+}
+
+#define SHP_TRY(x)                \
+  do {                            \
+    const int rc_ = (x);          \
+    if (rc_ != SHAMPOO_OK) return rc_; \
+  } while (0)
+
+// A small pool of equally sized stacks for the iterations.
+struct Pool {
+  float* buf[8];
+  bool used[8];
+  int n = 0;
+  float* get() {
+    for (int i = 0; i < n; ++i)
+      if (!used[i]) {
+        used[i] = true;
+        return buf[i];
+      }
+    return nullptr;
+  }
+  void put(float* p) {
+    for (int i = 0; i < n; ++i)
+      if (buf[i] == p) used[i] = false;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Workspace layouts.
+// ---------------------------------------------------------------------------
+struct NewtonWs {
+  Pool pool;
+  float* partials;
+};
+
+size_t newton_layout(Carver& c, int64_t nf, int B, int variant, NewtonWs* out) {
+  const int nbuf = (variant == SHAMPOO_CN) ? 7 : 5;
+  NewtonWs w;
+  w.pool.n = nbuf;
+  for (int i = 0; i < nbuf; ++i) {
+    w.pool.buf[i] = c.take<float>(stack_elems(nf, B));
+    w.pool.used[i] = false;
+  }
+  const int cnt = gemm_tiles(B) > ew_chunks(B) ? gemm_tiles(B) : ew_chunks(B);
+  w.partials = c.take<float>((size_t)nf * cnt);
+  if (out) *out = w;
+  return c.off;
+}
+
+struct ScaleWs {
+  float* w[2];
+  float* norm[2];
+  float* rq;
+  float* sumsq;
+};
+
+int pi_panel(int B) { return (B % 128 == 0) ? 128 : 64; }
+
+size_t scale_layout(Carver& c, int64_t nf, int B, ScaleWs* out) {
+  ScaleWs w;
+  const int np = B / pi_panel(B);
+  w.w[0] = c.take<float>((size_t)nf * B * kPiCols);
+  w.w[1] = c.take<float>((size_t)nf * B * kPiCols);
+  w.norm[0] = c.take<float>((size_t)nf * np * kPiCols);
+  w.norm[1] = c.take<float>((size_t)nf * np * kPiCols);
+  w.rq = c.take<float>((size_t)nf * np * kPiCols);
+  w.sumsq = c.take<float>((size_t)nf * ew_chunks(B));
+  if (out) *out = w;
+  return c.off;
+}
+
+struct ChebyWs {
+  float* as;
+  float* b[3];
+  uint16_t* as_t16;    // bf16 copy of A_s^T
+  uint16_t* b16[2];    // bf16 copies of the Clenshaw terms
+};
+
+size_t cheby_layout(Carver& c, int64_t nf, int B, int prec, ChebyWs* out) {
+  ChebyWs w;
+  w.as = c.take<float>(stack_elems(nf, B));
+  for (int i = 0; i < 3; ++i) w.b[i] = c.take<float>(stack_elems(nf, B));
+  w.as_t16 = nullptr;
+  w.b16[0] = w.b16[1] = nullptr;
+  if (prec == SHAMPOO_BF16_IN) {
+    w.as_t16 = c.take<uint16_t>(stack_elems(nf, B));
+    w.b16[0] = c.take<uint16_t>(stack_elems(nf, B));
+    w.b16[1] = c.take<uint16_t>(stack_elems(nf, B));
+  }
+  if (out) *out = w;
+  return c.off;
+}
+
+struct PrecondWs {
+  float* t1;
+  uint16_t* a16;   // bf16 X_L
+  uint16_t* b16;   // bf16 G^T (as rows), then X_R^T
+  uint16_t* t16;   // bf16 T1
+};
+
+size_t precond_layout(Carver& c, int64_t n, int B, int prec, PrecondWs* out) {
+  PrecondWs w;
+  w.t1 = nullptr;
+  w.a16 = w.b16 = w.t16 = nullptr;
+  if (prec == SHAMPOO_BF16_IN) {
+    w.a16 = c.take<uint16_t>(stack_elems(n, B));
+    w.b16 = c.take<uint16_t>(stack_elems(n, B));
+    w.t16 = c.take<uint16_t>(stack_elems(n, B));
+  } else {
+    w.t1 = c.take<float>(stack_elems(n, B));
+  }
+  if (out) *out = w;
+  return c.off;
+}
+
+struct AccumWs {
+  uint16_t* g16;   // bf16 G
+  uint16_t* gt16;  // bf16 G^T
+};
+
+size_t accum_layout(Carver& c, int64_t n, int B, int prec, AccumWs* out) {
+  AccumWs w;
+  w.g16 = w.gt16 = nullptr;
+  if (prec == SHAMPOO_BF16_IN) {
+    w.g16 = c.take<uint16_t>(stack_elems(n, B));
+    w.gt16 = c.take<uint16_t>(stack_elems(n, B));
+  }
+  if (out) *out = w;
+  return c.off;
+}
+
+// ---------------------------------------------------------------------------
+// Newton-DB.
+// ---------------------------------------------------------------------------
+
+// Where the last product of a pass goes.
+struct FinalOut {
+  float* x;                   // x_out, or nullptr: keep the result in a pool buffer
+  const shampoo_scale* sc;
+  const int32_t* status;
+  float pexp, extra;
+};
+
+EpiStore::Job final_job(const FinalOut& fo) {
+  EpiStore::Job j;
+  j.out = fo.x;
+  j.cin = nullptr;
+  j.alpha = 1.f;
+  j.beta = 0.f;
+  j.scale = fo.sc;
+  j.status = fo.status;
+  j.pexp = fo.pexp;
+  j.extra = fo.extra;
+  return j;
+}
+
+EpiStore::Job plain_job(float* out) {
+  EpiStore::Job j;
+  j.out = out;
+  j.cin = nullptr;
+  j.alpha = 1.f;
+  j.beta = 0.f;
+  j.scale = nullptr;
+  j.status = nullptr;
+  j.pexp = 0.f;
+  j.extra = 1.f;
+  return j;
+}
+
+struct NdbCtx {
+  int64_t nf;
+  int B;
+  int iters;
+  float* resid;
+  int ncols;
+  int32_t* status;
+  NewtonWs* ws;
+  hipStream_t st;
+};
+
+// One Newton-DB pass.  The prologue reads `src` and forms Y0 = a src + b I
+// (a, b per factor from `sc` when given, else ua/ub).  If `y0_in_src`, Y0 is
+// `src` itself (a = 1, b = 0) and is not copied.  A `src` that is a pool
+// buffer is owned by the pass and returned to the pool once it is dead.
+// `want_y` selects which iterate is the pass's result (Y if true, else Z).
+// With fo.x set the result is written to fo.x through the final epilogue;
+// else *result receives the pool buffer holding it.
+int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_scale* sc, float ua, float ub,
+             bool want_y, int pass, const FinalOut& fo, float** result) {
+  Pool& pool = c.ws->pool;
+  const int B = c.B;
+  const int64_t nf = c.nf;
+  float* Y = y0_in_src ? const_cast<float*>(src) : pool.get();
+  float* E = pool.get();
+  if (Y == nullptr || E == nullptr) return SHAMPOO_EWORKSPACE;
+  if (E == nullptr) return SHAMPOO_EWORKSPACE;
+  if (!y0_in_src) pool.put(const_cast<float*>(src));  // no-op for the caller's factors
+
+  EwArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = src;
+  a.out0 = y0_in_src ? nullptr : Y;
+  a.out1 = E;
+  a.partials = c.ws->partials;
+  a.sc = sc;
+  a.status = c.status;
+  a.ua = ua;
+  a.ub = ub;
+  a.p = 2.f;
+  a.B = B;
+  a.chunks = ew_chunks(B);
+  SHP_TRY(run_ew<EW_NDB_START>(a, nf, c.st));
+  SHP_TRY(run_resid(c.ws->partials, a.chunks, c.resid, c.ncols, pass * c.iters, c.status, nf, c.st));
+
+  const int tiles = gemm_tiles(B);
+  float* Z = E;  // Z_1 = E_0 (Z_0 = I)
+  // Iteration 1: Y_1 = Y_0 E_0.
+  if (c.iters == 1) {
+    if (want_y) {
+      if (fo.x) {
+        EpiStore::Job j = final_job(fo);
+        const float* A[1] = {Y};
+        const float* Bm[1] = {E};
+        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st));
+        *result = nullptr;
+      } else {
+        float* Yn = pool.get();
+        if (Yn == nullptr) return SHAMPOO_EWORKSPACE;
+        EpiStore::Job j = plain_job(Yn);
+        const float* A[1] = {Y};
+        const float* Bm[1] = {E};
+        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st));
+        *result = Yn;
+      }
+      pool.put(Y);
+      pool.put(E);
+    } else {
+      if (fo.x) {
+        EwArgs s;
+        memset(&s, 0, sizeof(s));
+        s.x = E;
+        s.out0 = fo.x;
+        s.sc = fo.sc;
+        s.status = fo.status;
+        s.pexp = fo.pexp;
+        s.extra = fo.extra;
+        s.p = 1.f;
+        s.B = B;
+        s.chunks = ew_chunks(B);
+        SHP_TRY(run_ew<EW_SCALE_COPY>(s, nf, c.st));
+        pool.put(E);
+        *result = nullptr;
+      } else {
+        *result = E;
+      }
+      pool.put(Y);
+    }
+    return SHAMPOO_OK;
+  }
+  {
+    float* Yn = pool.get();
+    if (Yn == nullptr) return SHAMPOO_EWORKSPACE;
+    EpiStore::Job j = plain_job(Yn);
+    const float* A[1] = {Y};
+    const float* Bm[1] = {E};
+    SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st));
+    pool.put(Y);
+    Y = Yn;
+  }
+  for (int it = 1; it < c.iters; ++it) {
+    // P = Z Y -> E = (3I - P)/2 and ||I - P||^2 partials.
+    float* En = pool.get();
+    if (En == nullptr) return SHAMPOO_EWORKSPACE;
+    {
+      EpiNdbE::Job j;
+      j.e = En;
+      j.partials = c.ws->partials;
+      j.tiles = tiles;
+      const float* A[1] = {Z};
+      const float* Bm[1] = {Y};
+      SHP_TRY(gemm_nn<EpiNdbE>(A, Bm, &j, 1, nf, B, c.st));
+      SHP_TRY(run_resid(c.ws->partials, tiles, c.resid, c.ncols, pass * c.iters + it, c.status, nf, c.st));
+    }
+    const bool last = (it == c.iters - 1);
+    if (!last) {
+      float* Yn = pool.get();
+      if (Yn == nullptr) return SHAMPOO_EWORKSPACE;
+      float* Zn = pool.get();
+      if (Zn == nullptr) return SHAMPOO_EWORKSPACE;
+      EpiStore::Job j[2] = {plain_job(Yn), plain_job(Zn)};
+      const float* A[2] = {Y, En};
+      const float* Bm[2] = {En, Z};
+      SHP_TRY(gemm_nn<EpiStore>(A, Bm, j, 2, nf, B, c.st));
+      pool.put(Y);
+      pool.put(Z);
+      pool.put(En);
+      Y = Yn;
+      Z = Zn;
+    } else {
+      float* dst = fo.x ? nullptr : pool.get();
+      if (!fo.x && dst == nullptr) return SHAMPOO_EWORKSPACE;
+      EpiStore::Job j = fo.x ? final_job(fo) : plain_job(dst);
+      const float* A[1] = {want_y ? Y : En};
+      const float* Bm[1] = {want_y ? En : Z};
+      SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st));
+      pool.put(Y);
+      pool.put(Z);
+      pool.put(En);
+      *result = dst;
+    }
+  }
+  return SHAMPOO_OK;
+}
+
+int newton_db(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, bool zchain, int iters,
+              float* x, float* resid, int32_t* status, NewtonWs* ws, hipStream_t st) {
+  NdbCtx c{nf, B, iters, resid, (p == 2 ? 1 : 2) * iters, status, ws, st};
+  FinalOut fo{x, sc, status, -1.f / (float)p, 1.f};
+  float* r1 = nullptr;
+  if (p == 2) return ndb_pass(c, F, false, sc, 0.f, 0.f, false, 0, fo, &r1);
+  FinalOut keep{nullptr, nullptr, nullptr, 0.f, 1.f};
+  if (!zchain) {
+    SHP_TRY(ndb_pass(c, F, false, sc, 0.f, 0.f, true, 0, keep, &r1));      // Y_1 ~ A_s^{1/2}
+    float* r2 = nullptr;
+    return ndb_pass(c, r1, true, nullptr, 1.f, 0.f, false, 1, fo, &r2);  // Z_2 ~ Y_1^{-1/2}
+  }
+  const double s2 = std::pow(1.5, (double)iters);
+  SHP_TRY(ndb_pass(c, F, false, sc, 0.f, 0.f, false, 0, keep, &r1));  // Z_1 ~ A_s^{-1/2}
+  FinalOut fz{x, sc, status, -0.25f, (float)std::sqrt(s2)};
+  float* r2 = nullptr;
+  return ndb_pass(c, r1, false, nullptr, (float)(1.0 / s2), 0.f, true, 1, fz, &r2);
+}
+
+// ---------------------------------------------------------------------------
+// Coupled Newton.
+// ---------------------------------------------------------------------------
+int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, int iters, float* x,
+                   float* resid, int32_t* status, NewtonWs* ws, hipStream_t st) {
+  Pool& pool = ws->pool;
+  float* M = pool.get();
+  if (M == nullptr) return SHAMPOO_EWORKSPACE;
+  float* C = pool.get();
+  if (C == nullptr) return SHAMPOO_EWORKSPACE;
+  EwArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = F;
+  a.out0 = M;
+  a.out1 = C;
+  a.partials = ws->partials;
+  a.sc = sc;
+  a.status = status;
+  a.p = (float)p;
+  a.B = B;
+  a.chunks = ew_chunks(B);
+  SHP_TRY(run_ew<EW_CN_START>(a, nf, st));
+  SHP_TRY(run_resid(ws->partials, a.chunks, resid, iters, 0, status, nf, st));
+  const float pexp = -1.f / (float)p;
+  if (iters == 1) {
+    EwArgs s;
+    memset(&s, 0, sizeof(s));
+    s.x = C;
+    s.out0 = x;
+    s.sc = sc;
+    s.status = status;
+    s.pexp = pexp;
+    s.extra = 1.f;
+    s.p = 1.f;
+    s.B = B;
+    s.chunks = ew_chunks(B);
+    return run_ew<EW_SCALE_COPY>(s, nf, st);
+  }
+  const int tiles = gemm_tiles(B);
+  float* X = nullptr;  // X_1 = C_0 (X_0 = I): first iteration has no X product
+  for (int it = 0; it < iters; ++it) {
+    const bool last = (it == iters - 1);
+    if (last) {
+      FinalOut fo{x, sc, status, pexp, 1.f};
+      EpiStore::Job j = final_job(fo);
+      const float* A[1] = {X};
+      const float* Bm[1] = {C};
+      return gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st);
+    }
+    // C^p by squaring, with X C in the same launch as the first square.
+    float* Cp = C;
+    float* Xn = nullptr;
+    if (it == 0) {
+      X = C;  // X_1 = C_0; C_0 stays alive as X
+    }
+    if (p >= 2) {
+      float* C2 = pool.get();
+      if (C2 == nullptr) return SHAMPOO_EWORKSPACE;
+      if (it > 0) {
+        Xn = pool.get();
+        if (Xn == nullptr) return SHAMPOO_EWORKSPACE;
+        EpiStore::Job j[2] = {plain_job(Xn), plain_job(C2)};
+        const float* A[2] = {X, C};
+        const float* Bm[2] = {C, C};
+        SHP_TRY(gemm_nn<EpiStore>(A, Bm, j, 2, nf, B, st));
+      } else {
+        EpiStore::Job j = plain_job(C2);
+        const float* A[1] = {C};
+        const float* Bm[1] = {C};
+        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st));
+      }
+      Cp = C2;
+      for (int q = 4; q <= p; q *= 2) {
+        float* Cq = pool.get();
+        if (Cq == nullptr) return SHAMPOO_EWORKSPACE;
+        EpiStore::Job j = plain_job(Cq);
+        const float* A[1] = {Cp};
+        const float* Bm[1] = {Cp};
+        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st));
+        pool.put(Cp);
+        Cp = Cq;
+      }
+    } else if (it > 0) {
+      Xn = pool.get();
+      if (Xn == nullptr) return SHAMPOO_EWORKSPACE;
+      EpiStore::Job j = plain_job(Xn);
+      const float* A[1] = {X};
+      const float* Bm[1] = {C};
+      SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st));
+    }
+    // M_{k+1} = C^p M_k, C_{k+1} = ((p+1) I - M_{k+1}) / p.
+    float* Mn = pool.get();
+    if (Mn == nullptr) return SHAMPOO_EWORKSPACE;
+    float* Cn = pool.get();
+    if (Cn == nullptr) return SHAMPOO_EWORKSPACE;
+    {
+      EpiCnM::Job j;
+      j.m = Mn;
+      j.c = Cn;
+      j.partials = ws->partials;
+      j.tiles = tiles;
+      j.p = (float)p;
+      const float* A[1] = {Cp};
+      const float* Bm[1] = {M};
+      SHP_TRY(gemm_nn<EpiCnM>(A, Bm, &j, 1, nf, B, st));
+      SHP_TRY(run_resid(ws->partials, tiles, resid, iters, it + 1, status, nf, st));
+    }
+    if (Cp != C) pool.put(Cp);
+    pool.put(M);
+    if (it > 0) {
+      pool.put(X);
+      pool.put(C);
+      X = Xn;
+    }
+    M = Mn;
+    C = Cn;
+  }
+  return SHAMPOO_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Chebyshev.
+// ---------------------------------------------------------------------------
+
+// Interpolant of x^{-1/p} at the degree+1 first-kind Chebyshev nodes of
+// [delta, 1 + delta], as coefficients of T_j(2 (x - delta) - 1), c_0 halved.
+void cheby_fit(int degree, int p, double delta, double* c) {
+  const int n = degree + 1;
+  const double pi = 3.14159265358979323846;
+  for (int j = 0; j < n; ++j) c[j] = 0.0;
+  for (int m = 0; m < n; ++m) {
+    const double th = pi * (m + 0.5) / n;
+    const double x = delta + 0.5 * (1.0 + std::cos(th));
+    const double fx = std::pow(x, -1.0 / p);
+    for (int j = 0; j < n; ++j) c[j] += fx * std::cos(j * th);
+  }
+  for (int j = 0; j < n; ++j) c[j] *= 2.0 / n;
+  c[0] *= 0.5;
+}
+
+int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, int degree, double delta,
+              int prec, float* x, int32_t* status, ChebyWs* ws, hipStream_t st) {
+  double c[257];
+  cheby_fit(degree, p, delta, c);
+  const float pexp = -1.f / (float)p;
+  EwArgs a;
+  memset(&a, 0, sizeof(a));
+  a.x = F;
+  a.sc = sc;
+  a.status = status;
+  a.p = (float)p;
+  a.B = B;
+  a.chunks = ew_chunks(B);
+  if (degree == 1) {
+    a.out0 = x;
+    a.c0 = (float)c[0];
+    a.c1 = (float)c[1];
+    a.pexp = pexp;
+    a.extra = 1.f;
+    return run_ew<EW_CHEBY_LINEAR>(a, nf, st);
+  }
+  a.out0 = ws->as;
+  a.out1 = ws->b[0];  // b_d
+  a.out2 = ws->b[1];  // b_{d-1}
+  a.c0 = (float)c[degree];
+  a.c1 = (float)c[degree - 1];
+  SHP_TRY(run_ew<EW_CHEBY_START>(a, nf, st));
+  const bool bf = (prec == SHAMPOO_BF16_IN);
+  int i2 = 0, i1 = 1, i0 = 2;  // ring slots of b_{j+2}, b_{j+1}, b_j
+  int s1 = 0;                  // bf16 slot holding b_{j+1}
+  if (bf) {
+    SHP_TRY(bf16_cast(ws->as, ws->as_t16, nf, B, true, st));
+    SHP_TRY(bf16_cast(ws->b[i1], ws->b16[s1], nf, B, false, st));
+  }
+  for (int j = degree - 2; j >= 0; --j) {
+    EpiClenshaw::Job e;
+    e.out = (j == 0) ? x : ws->b[i0];
+    e.out_bf16 = (bf && j > 0) ? ws->b16[s1 ^ 1] : nullptr;
+    e.b1 = ws->b[i1];
+    e.b2 = ws->b[i2];
+    e.cj = (float)c[j];
+    e.final = (j == 0) ? 1 : 0;
+    e.scale = sc;
+    e.status = status;
+    e.pexp = pexp;
+    if (bf) {
+      SHP_TRY(bf16_gemm_nt_clenshaw(ws->b16[s1], ws->as_t16, e, nf, B, st));
+      s1 ^= 1;
+    } else {
+      const float* A[1] = {ws->as};
+      const float* Bm[1] = {ws->b[i1]};
+      SHP_TRY(gemm_nn<EpiClenshaw>(A, Bm, &e, 1, nf, B, st));
+    }
+    const int t = i2;
+    i2 = i1;
+    i1 = i0;
+    i0 = t;
+  }
+  return SHAMPOO_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+int shampoo_abi_version(void) { return SHAMPOO_ABI_VERSION; }
+
+const char* shampoo_strerror(int code) {
+  switch (code) {
+    case SHAMPOO_OK: return "success";
+    case SHAMPOO_EINVAL: return "invalid argument (null pointer, negative count or parameter out of range)";
+    case SHAMPOO_EUNSUPPORTED: return "unsupported configuration (B must be a multiple of 64 in [64, 16384])";
+    case SHAMPOO_EWORKSPACE: return "workspace missing or smaller than shampoo_workspace_bytes";
+    case SHAMPOO_EHIP: return "HIP runtime error while launching a kernel";
+    default: return "unknown shampoo error code";
+  }
+}
+
+size_t shampoo_workspace_bytes(int op, int64_t count, int B, int variant_or_degree, int prec) {
+  if (count < 0 || !valid_B(B)) return 0;
+  if (prec != SHAMPOO_F32 && prec != SHAMPOO_BF16_IN) return 0;
+  Carver c(nullptr);
+  switch (op) {
+    case SHAMPOO_OP_ACCUMULATE: return accum_layout(c, count, B, prec, nullptr);
+    case SHAMPOO_OP_SCALE: return scale_layout(c, count, B, nullptr);
+    case SHAMPOO_OP_NEWTON:
+      if (variant_or_degree < SHAMPOO_NDB || variant_or_degree > SHAMPOO_CN) return 0;
+      return newton_layout(c, count, B, variant_or_degree, nullptr);
+    case SHAMPOO_OP_CHEBY: return cheby_layout(c, count, B, prec, nullptr);
+    case SHAMPOO_OP_PRECONDITION: return precond_layout(c, count, B, prec, nullptr);
+    default: return 0;
+  }
+}
+
+int shampoo_accumulate(const shampoo_block* g_blocks, int64_t nblocks, int B, float* factors, float alpha,
+                       float gamma, int prec, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (nblocks < 0) return SHAMPOO_EINVAL;
+  if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
+  if (prec != SHAMPOO_F32 && prec != SHAMPOO_BF16_IN) return SHAMPOO_EUNSUPPORTED;
+  if (prec == SHAMPOO_BF16_IN && (B % 128) != 0) return SHAMPOO_EUNSUPPORTED;
+  if (!std::isfinite(alpha) || !std::isfinite(gamma)) return SHAMPOO_EINVAL;
+  if (nblocks == 0) return SHAMPOO_OK;
+  if (g_blocks == nullptr || factors == nullptr) return SHAMPOO_EINVAL;
+  Carver cm(nullptr);
+  const size_t need = accum_layout(cm, nblocks, B, prec, nullptr);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return SHAMPOO_EWORKSPACE;
+  Carver c(ws);
+  AccumWs w;
+  accum_layout(c, nblocks, B, prec, &w);
+
+  EpiStore::Job jl;
+  jl.out = factors;
+  jl.cin = factors;
+  jl.alpha = gamma;
+  jl.beta = alpha;
+  jl.scale = nullptr;
+  jl.status = nullptr;
+  jl.pexp = 0.f;
+  jl.extra = 1.f;
+  EpiStore::Job jr = jl;
+  jr.out = factors + stack_elems(nblocks, B);
+  jr.cin = jr.out;
+  if (prec == SHAMPOO_BF16_IN) {
+    SHP_TRY(bf16_gather(g_blocks, nblocks, B, w.g16, w.gt16, stream));
+    SHP_TRY(bf16_gemm_nt_store(w.g16, w.g16, jl, nblocks, B, true, stream));
+    return bf16_gemm_nt_store(w.gt16, w.gt16, jr, nblocks, B, true, stream);
+  }
+  const Operand g = blocks(g_blocks);
+  // L = G G^T: A(m,k) = G[m][k], B(n,k) = G[n][k] -- both k-contiguous.
+  SHP_TRY((run_gemm<KCONTIG, KCONTIG, true, true, EpiStore>(&g, &g, &jl, 1, nblocks, B, true, stream)));
+  // R = G^T G: A(m,k) = G[k][m], B(n,k) = G[k][n] -- both mn-contiguous.
+  return run_gemm<MNCONTIG, MNCONTIG, true, true, EpiStore>(&g, &g, &jr, 1, nblocks, B, true, stream);
+}
+
+int shampoo_scale_power(const float* factors, int64_t nfactors, int B, float eps_rel, int mode, const float* v0,
+                        int r, int steps, float safety, shampoo_scale* scale_out, int32_t* status, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  if (nfactors < 0) return SHAMPOO_EINVAL;
+  if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
+  if (!(eps_rel >= 0.f) || !std::isfinite(eps_rel)) return SHAMPOO_EINVAL;
+  if (mode != SHAMPOO_SCALE_POWER && mode != SHAMPOO_SCALE_FROBENIUS) return SHAMPOO_EINVAL;
+  if (mode == SHAMPOO_SCALE_POWER) {
+    if (r < 1 || r > kPiCols || steps < 1 || steps > 10000) return SHAMPOO_EINVAL;
+    if (!(safety > 0.f) || !std::isfinite(safety)) return SHAMPOO_EINVAL;
+  }
+  if (nfactors == 0) return SHAMPOO_OK;
+  if (factors == nullptr || scale_out == nullptr || status == nullptr) return SHAMPOO_EINVAL;
+  if (mode == SHAMPOO_SCALE_POWER && v0 == nullptr) return SHAMPOO_EINVAL;
+  Carver cm(nullptr);
+  const size_t need = scale_layout(cm, nfactors, B, nullptr);
+  if (ws == nullptr || ws_bytes < need) return SHAMPOO_EWORKSPACE;
+  if ((uint64_t)nfactors > 0x7fffffffull / (uint64_t)(B / 64)) return SHAMPOO_EUNSUPPORTED;
+  Carver c(ws);
+  ScaleWs w;
+  scale_layout(c, nfactors, B, &w);
+
+  hipLaunchKernelGGL(trace_kernel, dim3((uint32_t)nfactors), dim3(256), 0, stream, factors, B, eps_rel, scale_out);
+  SHP_TRY(check_launch());
+  if (mode == SHAMPOO_SCALE_FROBENIUS) {
+    const int chunks = ew_chunks(B);
+    hipLaunchKernelGGL(sumsq_kernel, dim3((uint32_t)(nfactors * chunks)), dim3(256), 0, stream, factors,
+                       (int64_t)B * B, chunks, w.sumsq);
+    SHP_TRY(check_launch());
+    hipLaunchKernelGGL(frob_finalize_kernel, dim3((uint32_t)nfactors), dim3(64), 0, stream, w.sumsq, chunks, B,
+                       scale_out, status);
+    return check_launch();
+  }
+  const int panel = pi_panel(B);
+  PiArgs P;
+  memset(&P, 0, sizeof(P));
+  P.F = factors;
+  P.sc = scale_out;
+  P.B = B;
+  P.npanels = B / panel;
+  P.total = (uint32_t)(nfactors * P.npanels);
+  P.rq_out = w.rq;
+  for (int t = 0; t <= steps; ++t) {
+    P.vin = (t == 0) ? v0 : w.w[(t - 1) & 1];
+    P.ldv = (t == 0) ? r : kPiCols;
+    P.r = r;
+    P.wout = w.w[t & 1];
+    P.norm_in = (t == 0) ? nullptr : w.norm[(t - 1) & 1];
+    P.norm_out = w.norm[t & 1];
+    P.last = (t == steps) ? 1 : 0;
+    if (panel == 128)
+      hipLaunchKernelGGL(pi_step_kernel<128>, dim3(P.total), dim3(256), 0, stream, P);
+    else
+      hipLaunchKernelGGL(pi_step_kernel<64>, dim3(P.total), dim3(256), 0, stream, P);
+    SHP_TRY(check_launch());
+  }
+  hipLaunchKernelGGL(pi_finalize_kernel, dim3((uint32_t)nfactors), dim3(64), 0, stream, w.rq, P.npanels, r, safety,
+                     scale_out, status);
+  return check_launch();
+}
+
+int shampoo_invroot_newton(const float* factors, const shampoo_scale* scale, int64_t nfactors, int B, int p,
+                           int variant, int iters, float* x_out, float* resid_out, int32_t* status, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (nfactors < 0) return SHAMPOO_EINVAL;
+  if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
+  if (variant < SHAMPOO_NDB || variant > SHAMPOO_CN) return SHAMPOO_EINVAL;
+  if (iters < 1 || iters > 100) return SHAMPOO_EINVAL;
+  if (variant == SHAMPOO_CN) {
+    if (p != 1 && p != 2 && p != 4 && p != 8) return SHAMPOO_EUNSUPPORTED;
+  } else if (p != 2 && p != 4) {
+    return SHAMPOO_EUNSUPPORTED;
+  }
+  if (nfactors == 0) return SHAMPOO_OK;
+  if (factors == nullptr || scale == nullptr || x_out == nullptr || status == nullptr) return SHAMPOO_EINVAL;
+  Carver cm(nullptr);
+  const size_t need = newton_layout(cm, nfactors, B, variant, nullptr);
+  if (ws == nullptr || ws_bytes < need) return SHAMPOO_EWORKSPACE;
+  Carver c(ws);
+  NewtonWs w;
+  newton_layout(c, nfactors, B, variant, &w);
+  if (variant == SHAMPOO_CN)
+    return coupled_newton(factors, scale, nfactors, B, p, iters, x_out, resid_out, status, &w, stream);
+  return newton_db(factors, scale, nfactors, B, p, variant == SHAMPOO_NDB_Z, iters, x_out, resid_out, status, &w,
+                   stream);
+}
+
+int shampoo_invroot_cheby(const float* factors, const shampoo_scale* scale, int64_t nfactors, int B, int p,
+                          int degree, double interval_eps, int prec, float* x_out, int32_t* status, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  if (nfactors < 0) return SHAMPOO_EINVAL;
+  if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
+  if (p < 1 || p > 64) return SHAMPOO_EINVAL;
+  if (degree < 1 || degree > 256) return SHAMPOO_EINVAL;
+  if (!(interval_eps >= 0.0) || !std::isfinite(interval_eps)) return SHAMPOO_EINVAL;
+  if (prec != SHAMPOO_F32 && prec != SHAMPOO_BF16_IN) return SHAMPOO_EUNSUPPORTED;
+  if (prec == SHAMPOO_BF16_IN && (B % 128) != 0) return SHAMPOO_EUNSUPPORTED;
+  if (nfactors == 0) return SHAMPOO_OK;
+  if (factors == nullptr || scale == nullptr || x_out == nullptr || status == nullptr) return SHAMPOO_EINVAL;
+  Carver cm(nullptr);
+  const size_t need = cheby_layout(cm, nfactors, B, prec, nullptr);
+  if (ws == nullptr || ws_bytes < need) return SHAMPOO_EWORKSPACE;
+  Carver c(ws);
+  ChebyWs w;
+  cheby_layout(c, nfactors, B, prec, &w);
+  return chebyshev(factors, scale, nfactors, B, p, degree, interval_eps, prec, x_out, status, &w, stream);
+}
+
+int shampoo_precondition(const float* x_roots, const shampoo_block* g_blocks, int64_t nblocks, int B,
+                         const shampoo_block* u_blocks, int prec, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (nblocks < 0) return SHAMPOO_EINVAL;
+  if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
+  if (prec != SHAMPOO_F32 && prec != SHAMPOO_BF16_IN) return SHAMPOO_EUNSUPPORTED;
+  if (prec == SHAMPOO_BF16_IN && (B % 128) != 0) return SHAMPOO_EUNSUPPORTED;
+  if (nblocks == 0) return SHAMPOO_OK;
+  if (x_roots == nullptr || g_blocks == nullptr || u_blocks == nullptr) return SHAMPOO_EINVAL;
+  Carver cm(nullptr);
+  const size_t need = precond_layout(cm, nblocks, B, prec, nullptr);
+  if (ws == nullptr || ws_bytes < need) return SHAMPOO_EWORKSPACE;
+  Carver c(ws);
+  PrecondWs w;
+  precond_layout(c, nblocks, B, prec, &w);
+  const float* XL = x_roots;
+  const float* XR = x_roots + stack_elems(nblocks, B);
+  if (prec == SHAMPOO_BF16_IN) {
+    // T1 = X_L G: NT form with rows of G^T; U = T1 X_R: NT form with rows of X_R^T.
+    SHP_TRY(bf16_cast(XL, w.a16, nblocks, B, false, stream));
+    SHP_TRY(bf16_gather(g_blocks, nblocks, B, nullptr, w.b16, stream));
+    SHP_TRY(bf16_gemm_nt_bf16out(w.a16, w.b16, w.t16, nblocks, B, stream));
+    SHP_TRY(bf16_cast(XR, w.b16, nblocks, B, true, stream));
+    return bf16_gemm_nt_desc(w.t16, w.b16, u_blocks, nblocks, B, stream);
+  }
+  // T1 = X_L G: B(n,k) = G[k][n] -- mn-contiguous through descriptors.
+  EpiStore::Job j = plain_job(w.t1);
+  const Operand a = dense(XL);
+  const Operand g = blocks(g_blocks);
+  SHP_TRY((run_gemm<KCONTIG, MNCONTIG, false, true, EpiStore>(&a, &g, &j, 1, nblocks, B, false, stream)));
+  // U = T1 X_R, written through the output descriptors.
+  EpiStoreDesc::Job ju{u_blocks};
+  const Operand t = dense(w.t1);
+  const Operand xr = dense(XR);
+  return run_gemm<KCONTIG, MNCONTIG, false, false, EpiStoreDesc>(&t, &xr, &ju, 1, nblocks, B, false, stream);
+}
+
+}  // extern "C"

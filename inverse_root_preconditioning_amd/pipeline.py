@@ -1,0 +1,224 @@
+"""Torch-tensor layer over the C ABI: descriptor tables, workspaces and the
+per-step driver.  PyTorch provides device memory and the stream; all the
+arithmetic runs in the HIP library (see capi).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import capi
+
+F32 = capi.F32
+BF16_IN = capi.BF16_IN
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def _check_f32_cuda(t, name, shape=None):
+    if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class BlockTable:
+    """Device array of shampoo_block descriptors (24 bytes each) plus the
+    tensors it points into (kept alive with the table)."""
+
+    def __init__(self, entries, B, device=None):
+        n = len(entries)
+        arr = np.zeros((max(n, 1), 3), dtype=np.int64)
+        keep = []
+        for i, (t, r0, c0, rows, cols) in enumerate(entries):
+            if t.dtype != torch.float32 or t.dim() != 2 or t.stride(1) != 1:
+                raise ValueError("blocks must come from row-major float32 2D tensors")
+            if not (0 <= rows <= B and 0 <= cols <= B):
+                raise ValueError("block larger than B")
+            if r0 < 0 or c0 < 0 or r0 + rows > t.shape[0] or c0 + cols > t.shape[1]:
+                raise ValueError("block outside its tensor")
+            ld = t.stride(0)
+            arr[i, 0] = t.data_ptr() + 4 * (r0 * ld + c0)
+            arr[i, 1] = ld
+            arr[i, 2] = int(rows) | (int(cols) << 32)
+            keep.append(t)
+        self.n = n
+        self.B = B
+        self._keep = keep
+        dev = device if device is not None else (entries[0][0].device if n else torch.device("cuda"))
+        self.tensor = torch.from_numpy(arr).to(dev)
+
+    @property
+    def ptr(self):
+        return self.tensor.data_ptr()
+
+    @classmethod
+    def from_stack(cls, stack):
+        """One full B x B block per item of a [n, B, B] tensor."""
+        n, B, _ = stack.shape
+        return cls([(stack[i], 0, 0, B, B) for i in range(n)], B, stack.device)
+
+    @classmethod
+    def from_layers(cls, tensors, B):
+        """Row-major B x B tiling of each 2D tensor, tensors in order (edge
+        blocks may be partial)."""
+        entries = []
+        for t in tensors:
+            m, n = t.shape
+            for r0 in range(0, m, B):
+                for c0 in range(0, n, B):
+                    entries.append((t, r0, c0, min(B, m - r0), min(B, n - c0)))
+        return cls(entries, B, tensors[0].device if tensors else None)
+
+
+class Workspace:
+    """Grow-only scratch buffer (uint8 CUDA tensor)."""
+
+    def __init__(self, device="cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes):
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf.data_ptr(), self.buf.numel()
+
+
+def accumulate(table, factors, alpha, gamma, prec=F32, ws=None, stream=None):
+    n, B = table.n, table.B
+    _check_f32_cuda(factors, "factors", (2 * n, B, B))
+    ws = ws or Workspace(factors.device)
+    need = capi.shampoo_workspace_bytes(capi.OP_ACCUMULATE, n, B, 0, prec)
+    wp, wb = ws.get(need) if need else (0, 0)
+    capi.check(capi.shampoo_accumulate(table.ptr, n, B, factors.data_ptr(), alpha, gamma, prec, wp, wb,
+                                       _stream(stream)), "shampoo_accumulate")
+
+
+def new_scale(nf, device):
+    """(scale [nf, 4] float32: c, eps, lambda, trace; status [nf] int32)."""
+    return (torch.zeros((nf, 4), dtype=torch.float32, device=device),
+            torch.zeros((nf,), dtype=torch.int32, device=device))
+
+
+def scale_power(factors, eps_rel, mode, v0, steps, safety, scale, status, ws=None, stream=None):
+    nf, B, _ = factors.shape
+    _check_f32_cuda(factors, "factors")
+    r = 0
+    if mode == capi.SCALE_POWER:
+        _check_f32_cuda(v0, "v0")
+        if v0.shape[0] != nf or v0.shape[1] != B:
+            raise ValueError("v0 must be [nfactors, B, r]")
+        r = v0.shape[2]
+    ws = ws or Workspace(factors.device)
+    wp, wb = ws.get(capi.shampoo_workspace_bytes(capi.OP_SCALE, nf, B, 0, F32))
+    capi.check(capi.shampoo_scale_power(factors.data_ptr(), nf, B, eps_rel, mode, _ptr(v0), r, steps, safety,
+                                        scale.data_ptr(), status.data_ptr(), wp, wb, _stream(stream)),
+               "shampoo_scale_power")
+
+
+def invroot_newton(factors, scale, p, variant, iters, x_out, status, resid_out=None, ws=None, stream=None):
+    nf, B, _ = factors.shape
+    _check_f32_cuda(factors, "factors")
+    _check_f32_cuda(x_out, "x_out", factors.shape)
+    ws = ws or Workspace(factors.device)
+    wp, wb = ws.get(capi.shampoo_workspace_bytes(capi.OP_NEWTON, nf, B, variant, F32))
+    capi.check(capi.shampoo_invroot_newton(factors.data_ptr(), scale.data_ptr(), nf, B, p, variant, iters,
+                                           x_out.data_ptr(), _ptr(resid_out), status.data_ptr(), wp, wb,
+                                           _stream(stream)), "shampoo_invroot_newton")
+
+
+def invroot_cheby(factors, scale, p, degree, interval_eps, prec, x_out, status, ws=None, stream=None):
+    nf, B, _ = factors.shape
+    _check_f32_cuda(factors, "factors")
+    _check_f32_cuda(x_out, "x_out", factors.shape)
+    ws = ws or Workspace(factors.device)
+    wp, wb = ws.get(capi.shampoo_workspace_bytes(capi.OP_CHEBY, nf, B, degree, prec))
+    capi.check(capi.shampoo_invroot_cheby(factors.data_ptr(), scale.data_ptr(), nf, B, p, degree, interval_eps,
+                                          prec, x_out.data_ptr(), status.data_ptr(), wp, wb, _stream(stream)),
+               "shampoo_invroot_cheby")
+
+
+def precondition(x_roots, g_table, u_table, prec=F32, ws=None, stream=None):
+    n, B = g_table.n, g_table.B
+    _check_f32_cuda(x_roots, "x_roots", (2 * n, B, B))
+    if u_table.n != n:
+        raise ValueError("output table size differs from the gradient table")
+    ws = ws or Workspace(x_roots.device)
+    need = capi.shampoo_workspace_bytes(capi.OP_PRECONDITION, n, B, 0, prec)
+    wp, wb = ws.get(need)
+    capi.check(capi.shampoo_precondition(x_roots.data_ptr(), g_table.ptr, n, B, u_table.ptr, prec, wp, wb,
+                                         _stream(stream)), "shampoo_precondition")
+
+
+@dataclass
+class StepConfig:
+    """One optimizer step of the block preconditioner (defaults: the pages'
+    Newton-DB with power-iteration scaling)."""
+    B: int
+    beta: float = 0.95          # EMA factor: alpha = beta, gamma = 1 - beta
+    eps_rel: float = 1e-12      # damping eps = eps_rel tr(F) / B
+    scale_mode: int = capi.SCALE_POWER
+    pi_steps: int = 20
+    pi_starts: int = 32
+    safety: float = 2.0
+    solver: str = "newton"      # "newton" or "cheby"
+    variant: int = capi.NDB
+    iters: int = 10
+    p: int = 4
+    degree: int = 24
+    interval_eps: float = 1e-12
+    prec: int = F32
+    keep_resid: bool = False
+
+
+@dataclass
+class ShampooBlocks:
+    """State and workspaces for a fixed set of gradient blocks."""
+    cfg: StepConfig
+    nblocks: int
+    device: object = "cuda"
+    factors: torch.Tensor = field(init=False)
+    roots: torch.Tensor = field(init=False)
+
+    def __post_init__(self):
+        B, n, dev = self.cfg.B, self.nblocks, self.device
+        self.factors = torch.zeros((2 * n, B, B), dtype=torch.float32, device=dev)
+        self.roots = torch.empty((2 * n, B, B), dtype=torch.float32, device=dev)
+        self.scale, self.status = new_scale(2 * n, dev)
+        self.resid = None
+        if self.cfg.keep_resid and self.cfg.solver == "newton":
+            passes = 1 if (self.cfg.p == 2 or self.cfg.variant == capi.CN) else 2
+            self.resid = torch.zeros((2 * n, passes * self.cfg.iters), dtype=torch.float32, device=dev)
+        self.ws = {k: Workspace(dev) for k in ("acc", "scale", "root", "pre")}
+        self.v0 = None
+
+    def set_start_vectors(self, v0):
+        _check_f32_cuda(v0, "v0", (2 * self.nblocks, self.cfg.B, v0.shape[2]))
+        self.v0 = v0
+
+    def step(self, g_table, u_table, stream=None):
+        c = self.cfg
+        accumulate(g_table, self.factors, c.beta, 1.0 - c.beta, c.prec, self.ws["acc"], stream)
+        self.update_roots(stream)
+        precondition(self.roots, g_table, u_table, c.prec, self.ws["pre"], stream)
+
+    def update_roots(self, stream=None):
+        c = self.cfg
+        scale_power(self.factors, c.eps_rel, c.scale_mode, self.v0, c.pi_steps, c.safety, self.scale,
+                    self.status, self.ws["scale"], stream)
+        if c.solver == "newton":
+            invroot_newton(self.factors, self.scale, c.p, c.variant, c.iters, self.roots, self.status,
+                           self.resid, self.ws["root"], stream)
+        else:
+            invroot_cheby(self.factors, self.scale, c.p, c.degree, c.interval_eps, c.prec, self.roots,
+                          self.status, self.ws["root"], stream)

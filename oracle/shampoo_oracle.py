@@ -336,9 +336,12 @@ def invroot(F, sc, method, iters=10, p=4, degree=24, delta=1e-12, chaining="Y"):
     c = sc["c"]
     A_s = damped(F, sc["eps"]) / c
     if method == "ndb":
-        if p != 4:
-            raise ValueError("two chained Newton-DB passes give p = 4")
-        X, _ = invroot_newton_db(A_s, iters, chaining)
+        if p == 2:  # one pass: Z tends to A_s^{-1/2}
+            X = newton_db_pass(A_s, iters)[1]
+        elif p == 4:
+            X, _ = invroot_newton_db(A_s, iters, chaining)
+        else:
+            raise ValueError("Newton-DB gives p = 2 (one pass) or p = 4 (two chained passes)")
     elif method == "cn":
         X = invroot_coupled_newton(A_s, p, iters)
     elif method == "cheby":

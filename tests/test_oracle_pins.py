@@ -353,3 +353,11 @@ def test_cheby_end_to_end_against_exact_and_lapack():
     poly = np.polynomial.chebyshev.chebval(2 * w - 1, c48)
     ref = sc["c"] ** -0.25 * (Q * poly) @ Q.T
     assert O.relative_frobenius(O.invroot(A, sc, "cheby", degree=48, delta=0.0), ref) <= 1e-12
+
+
+def test_ndb_single_pass_is_inverse_square_root():
+    A, _, _ = rand_spd(17, 12, 20.0)
+    V0 = np.random.default_rng(18).standard_normal((12, 4))
+    sc = O.scale_factor(A, 0.0, "power", V0, 30)
+    X = O.invroot(A, sc, "ndb", iters=30, p=2)
+    assert O.relative_frobenius(X, O.invroot_exact(A, 2)) <= 1e-12

@@ -1,0 +1,292 @@
+"""Stage-by-stage parity of the HIP path (through the C ABI) with the float64
+oracle on seeded inputs, at sizes that span several tiles, plus the edge
+cases of the method.  Tolerances: relative Frobenius per factor <= 1e-4 for
+fp32 paths and <= 2e-2 for bf16-input paths."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import shampoo_oracle as O
+from inverse_root_preconditioning_amd import capi
+from inverse_root_preconditioning_amd import pipeline as PL
+from inverse_root_preconditioning_amd import workloads as W
+
+from gpu_helpers import (TOL_BF16, TOL_F32, dev, gpu_roots, gpu_scale, host, oracle_root, oracle_scale,
+                         report)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    capi.load()
+    torch.manual_seed(0)
+
+
+def grads(key, n, B, std=1.0):
+    return np.stack([(W.rng(W.TAG_EDGE, key, i).standard_normal((B, B)) * std).astype(np.float32)
+                     for i in range(n)])
+
+
+# ---------------------------------------------------------------------------
+# accumulate
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B", [64, 128, 192, 256])
+def test_accumulate_gram_matches_oracle(B):
+    n = 3
+    G = grads(1, n, B, 0.02)
+    g = dev(G)
+    table = PL.BlockTable.from_stack(g)
+    F = torch.zeros((2 * n, B, B), dtype=torch.float32, device="cuda")
+    PL.accumulate(table, F, 0.0, 1.0)
+    out = host(F)
+    for i in range(n):
+        L, R = O.accumulate(np.zeros((B, B)), np.zeros((B, B)), G[i], 0.0, 1.0)
+        el, er = O.relative_frobenius(out[i], L), O.relative_frobenius(out[n + i], R)
+        assert el <= 1e-5 and er <= 1e-5, (el, er)
+        assert np.array_equal(out[i], out[i].T) and np.array_equal(out[n + i], out[n + i].T)
+    report("accumulate_gram", B=B, err=max(el, er))
+
+
+def test_accumulate_ema_ragged_blocks():
+    """Partial edge blocks (a 300 x 200 and a 128 x 70 gradient at B = 128),
+    misaligned rows (ld = 70) and an EMA on top of an existing state."""
+    B = 128
+    A1 = W.ragged_gradients(2, [(300, 200)], 0.5)[0]
+    A2 = W.ragged_gradients(3, [(128, 70)], 0.5)[0]
+    t1, t2 = dev(A1), dev(A2)
+    table = PL.BlockTable.from_layers([t1, t2], B)
+    n = table.n
+    assert n == 3 * 2 + 1
+    prev = grads(4, 2 * n, B, 0.1)
+    prevF = np.einsum("nij,nkj->nik", prev, prev).astype(np.float32)  # symmetric PSD start
+    F = dev(prevF)
+    PL.accumulate(table, F, 0.9, 0.1)
+    out = host(F)
+    blocks = []
+    for t in (A1, A2):
+        m, k = t.shape
+        for r0 in range(0, m, B):
+            for c0 in range(0, k, B):
+                blocks.append(O.pad_block(t[r0:r0 + B, c0:c0 + B], B))
+    err = 0.0
+    for i, Gb in enumerate(blocks):
+        L, R = O.accumulate(prevF[i], prevF[n + i], Gb, 0.9, 0.1)
+        err = max(err, O.relative_frobenius(out[i], L), O.relative_frobenius(out[n + i], R))
+    assert err <= 1e-5
+    report("accumulate_ema_ragged", err=err)
+
+
+def test_accumulate_bf16_input():
+    B, n = 256, 4
+    G = grads(5, n, B, 0.02)
+    g = dev(G)
+    F = torch.zeros((2 * n, B, B), dtype=torch.float32, device="cuda")
+    PL.accumulate(PL.BlockTable.from_stack(g), F, 0.0, 1.0, prec=capi.BF16_IN)
+    out = host(F)
+    err = 0.0
+    for i in range(n):
+        L, R = O.accumulate(np.zeros((B, B)), np.zeros((B, B)), G[i], 0.0, 1.0)
+        err = max(err, O.relative_frobenius(out[i], L), O.relative_frobenius(out[n + i], R))
+    assert err <= TOL_BF16
+    report("accumulate_bf16", err=err)
+
+
+# ---------------------------------------------------------------------------
+# scale
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,r", [(64, 32), (192, 32), (256, 7)])
+def test_scale_power_matches_oracle(B, r):
+    nf = 6
+    F = W.spd_factors(10 + B, nf, B, cond=1e4) * np.float32(3.0)
+    V0 = W.start_vectors(9, nf, B, r)
+    sc, st = gpu_scale(dev(F), 1e-3, capi.SCALE_POWER, dev(V0), 20, 2.0)
+    s, stt = host(sc), host(st)
+    err = 0.0
+    for i in range(nf):
+        o = oracle_scale(F[i], 1e-3, capi.SCALE_POWER, V0[i])
+        assert stt[i] == o["status"] == 0
+        for k, key in enumerate(("c", "eps", "lam", "trace")):
+            e = abs(s[i, k] - o[key]) / abs(o[key])
+            err = max(err, e)
+            assert e <= 2e-5, (key, s[i, k], o[key])
+    report("scale_power", B=B, r=r, err=err)
+
+
+def test_scale_frobenius_matches_oracle():
+    nf, B = 5, 128
+    F = W.spd_factors(20, nf, B, cond=1e2)
+    sc, st = gpu_scale(dev(F), 1e-2, capi.SCALE_FROBENIUS)
+    s = host(sc)
+    for i in range(nf):
+        o = oracle_scale(F[i], 1e-2, capi.SCALE_FROBENIUS, None)
+        assert abs(s[i, 0] - o["c"]) / o["c"] <= 1e-5
+        assert abs(s[i, 3] - o["trace"]) / o["trace"] <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# inverse roots
+# ---------------------------------------------------------------------------
+
+NEWTON_CASES = [
+    (capi.NDB, 4, 1), (capi.NDB, 4, 2), (capi.NDB, 4, 6), (capi.NDB_Z, 4, 1), (capi.NDB_Z, 4, 6),
+    (capi.NDB, 2, 5), (capi.CN, 4, 1), (capi.CN, 4, 2), (capi.CN, 4, 8), (capi.CN, 1, 6), (capi.CN, 2, 6),
+    (capi.CN, 8, 6),
+]
+
+
+@pytest.mark.parametrize("B", [64, 256])
+@pytest.mark.parametrize("variant,p,iters", NEWTON_CASES)
+def test_newton_matches_oracle(B, variant, p, iters):
+    nf = 4
+    F = W.spd_factors(30 + B, nf, B, cond=1e3)
+    V0 = W.start_vectors(31, nf, B)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    X, R = gpu_roots(Fd, sc, st, "newton", iters=iters, p=p, variant=variant, resid=True)
+    Xh, Rh = host(X), host(R)
+    err = 0.0
+    for i in range(nf):
+        o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
+        ref = oracle_root(F[i], o, "newton", iters=iters, p=p, variant=variant)
+        err = max(err, O.relative_frobenius(Xh[i], ref))
+    assert err <= TOL_F32, err
+    assert np.all(Rh >= 0.0) and np.all(np.isfinite(Rh))
+    report("newton", B=B, variant=variant, p=p, iters=iters, err=err)
+
+
+def test_newton_db_residuals_match_oracle():
+    nf, B, k = 3, 128, 5
+    F = W.spd_factors(40, nf, B, cond=1e2)
+    V0 = W.start_vectors(41, nf, B)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    _, R = gpu_roots(Fd, sc, st, "newton", iters=k, p=4, variant=capi.NDB, resid=True)
+    Rh = host(R)
+    for i in range(nf):
+        o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
+        A_s = O.damped(F[i], o["eps"]) / o["c"]
+        _, res = O.invroot_newton_db(A_s, k, "Y")
+        assert np.allclose(Rh[i], res, rtol=1e-3, atol=1e-5), (Rh[i], res)
+
+
+@pytest.mark.parametrize("B", [64, 128])
+@pytest.mark.parametrize("degree", [1, 2, 3, 16, 32])
+def test_chebyshev_f32_matches_oracle(B, degree):
+    nf = 4
+    F = W.spd_factors(50 + B, nf, B, cond=1e4)
+    V0 = W.start_vectors(51, nf, B)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    X, _ = gpu_roots(Fd, sc, st, "cheby", degree=degree)
+    Xh = host(X)
+    err = 0.0
+    for i in range(nf):
+        o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
+        err = max(err, O.relative_frobenius(Xh[i], oracle_root(F[i], o, "cheby", degree=degree)))
+    assert err <= TOL_F32, err
+    report("cheby_f32", B=B, degree=degree, err=err)
+
+
+@pytest.mark.parametrize("degree", [2, 16, 24])
+def test_chebyshev_bf16_matches_oracle(degree):
+    nf, B = 4, 256
+    F = W.spd_factors(60, nf, B, cond=1e4)
+    V0 = W.start_vectors(61, nf, B)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    X, _ = gpu_roots(Fd, sc, st, "cheby", degree=degree, prec=capi.BF16_IN)
+    Xh = host(X)
+    err = 0.0
+    for i in range(nf):
+        o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
+        err = max(err, O.relative_frobenius(Xh[i], oracle_root(F[i], o, "cheby", degree=degree)))
+    assert err <= TOL_BF16, err
+    report("cheby_bf16", degree=degree, err=err)
+
+
+# ---------------------------------------------------------------------------
+# precondition
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("prec,tol", [(capi.F32, 1e-5), (capi.BF16_IN, TOL_BF16)])
+def test_precondition_ragged(prec, tol):
+    B = 128
+    A1 = W.ragged_gradients(7, [(260, 300)], 1.0)[0]
+    t1 = dev(A1)
+    gt = PL.BlockTable.from_layers([t1], B)
+    n = gt.n
+    X = np.concatenate([W.spd_factors(70, n, B, cond=10.0), W.spd_factors(71, n, B, cond=10.0)])
+    U = torch.full_like(t1, float("nan"))
+    ut = PL.BlockTable.from_layers([U], B)
+    PL.precondition(dev(X), gt, ut, prec=prec)
+    Uh = host(U)
+    assert np.all(np.isfinite(Uh)), "some part of U was not written"
+    err = 0.0
+    i = 0
+    for r0 in range(0, A1.shape[0], B):
+        for c0 in range(0, A1.shape[1], B):
+            g = O.pad_block(A1[r0:r0 + B, c0:c0 + B], B)
+            ref = O.precondition(X[i], g, X[n + i])
+            rows, cols = min(B, A1.shape[0] - r0), min(B, A1.shape[1] - c0)
+            err = max(err, O.relative_frobenius(Uh[r0:r0 + rows, c0:c0 + cols], ref[:rows, :cols]))
+            i += 1
+    assert err <= tol, err
+    report("precondition", prec=prec, err=err)
+
+
+# ---------------------------------------------------------------------------
+# degenerate factors, empty input, determinism
+# ---------------------------------------------------------------------------
+
+def test_degenerate_factors():
+    B = 64
+    good = W.spd_factors(80, 1, B, cond=10.0)[0]
+    zero = np.zeros((B, B), np.float32)
+    neg = -good
+    bad = good.copy()
+    bad[3, 5] = np.nan
+    F = np.stack([good, zero, neg, bad])
+    V0 = W.start_vectors(81, 4, B)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 1e-12, capi.SCALE_POWER, dev(V0))
+    s = host(st)
+    for i in range(4):
+        assert s[i] == oracle_scale(F[i], 1e-12, capi.SCALE_POWER, V0[i])["status"], (i, s)
+    assert s[0] == 0 and s[1] == capi.BLK_ZERO and s[2] == capi.BLK_NONPOS_RQ and s[3] & capi.BLK_NONFINITE
+    for method in ("newton", "cheby"):
+        X, _ = gpu_roots(Fd, sc, st, method, iters=4, degree=8)
+        Xh = host(X)
+        assert np.array_equal(Xh[1], np.eye(B)) and np.array_equal(Xh[2], np.eye(B))
+        assert np.all(np.isfinite(Xh[0])) and not np.all(np.isfinite(Xh[3]))
+    s2 = host(st)
+    assert s2[3] & capi.BLK_NONFINITE
+
+
+def test_empty_input_is_noop():
+    F = torch.zeros((0, 64, 64), dtype=torch.float32, device="cuda")
+    sc, st = PL.new_scale(0, "cuda")
+    ws = PL.Workspace()
+    p, nb = ws.get(256)
+    assert capi.shampoo_invroot_newton(F.data_ptr(), sc.data_ptr(), 0, 64, 4, capi.NDB, 3, F.data_ptr(), 0,
+                                       st.data_ptr(), p, nb, 0) == capi.OK
+
+
+def test_repeat_runs_are_bitwise_identical():
+    nf, B = 6, 256
+    F = W.spd_factors(90, nf, B, cond=1e5)
+    V0 = W.start_vectors(91, nf, B)
+    Fd, Vd = dev(F), dev(V0)
+    outs = []
+    for _ in range(2):
+        sc, st = gpu_scale(Fd, 1e-12, capi.SCALE_POWER, Vd)
+        X, R = gpu_roots(Fd, sc, st, "newton", iters=7, variant=capi.NDB, resid=True)
+        outs.append((host(sc), host(X), host(R)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
