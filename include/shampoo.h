@@ -231,6 +231,27 @@ const char* shampoo_strerror(int code);
 /* SHAMPOO_ABI_VERSION of the built library. */
 int shampoo_abi_version(void);
 
+/* Kernel families for shampoo_timing_hook. */
+enum {
+  SHAMPOO_TIME_OFF = 0,
+  SHAMPOO_TIME_NDB_PAIR = 1,   /* Newton-DB updates Y E and E Z, launched together (2 products) */
+  SHAMPOO_TIME_NDB_P = 2,      /* Newton-DB product Z Y with the E = (3I - P)/2 epilogue */
+  SHAMPOO_TIME_CLENSHAW = 3    /* one Clenshaw product A_s b (fp32 or bf16) */
+};
+
+/*
+ * shampoo_timing_hook -- measurement instrumentation (not part of the method).
+ * While enabled, each launch of kernel family `family` made by any later call
+ * records events[2 i] just before and events[2 i + 1] just after the launch on
+ * that call's stream, for i < capacity; further launches are not recorded.
+ * `events` are caller-created HIP events (2 * capacity of them) that must
+ * outlive the recorded launches.  family = SHAMPOO_TIME_OFF disables the hook.
+ * The hook is process-wide and not thread-safe; enabling it resets the count.
+ * shampoo_timing_count returns how many launches have been recorded.
+ */
+int shampoo_timing_hook(int family, hipEvent_t* events, int capacity);
+int shampoo_timing_count(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,8 +59,16 @@ class ShampooError(RuntimeError):
         super().__init__(f"{where}: {strerror(code)} (code {code})")
 
 
+# Timing-hook kernel families
+TIME_OFF = 0
+TIME_NDB_PAIR = 1
+TIME_NDB_P = 2
+TIME_CLENSHAW = 3
+
 _SIGNATURES = {
     "shampoo_abi_version": (c_int, []),
+    "shampoo_timing_hook": (c_int, [c_int, c_void_p, c_int]),
+    "shampoo_timing_count": (c_int, []),
     "shampoo_strerror": (ctypes.c_char_p, [c_int]),
     "shampoo_workspace_bytes": (c_size_t, [c_int, c_int64, c_int, c_int, c_int]),
     "shampoo_accumulate": (c_int, [c_void_p, c_int64, c_int, c_void_p, c_float, c_float, c_int,
@@ -147,3 +155,11 @@ def shampoo_invroot_cheby(factors, scale, nfactors, B, p, degree, interval_eps, 
 
 def shampoo_precondition(x_roots, g_blocks, nblocks, B, u_blocks, prec, ws, ws_bytes, stream):
     return load().shampoo_precondition(x_roots, g_blocks, nblocks, B, u_blocks, prec, ws, ws_bytes, stream)
+
+
+def shampoo_timing_hook(family, events, capacity):
+    return load().shampoo_timing_hook(family, events, capacity)
+
+
+def shampoo_timing_count():
+    return load().shampoo_timing_count()

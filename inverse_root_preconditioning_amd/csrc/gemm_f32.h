@@ -307,6 +307,10 @@ struct EpiStore {
   };
 };
 
+// The two updates Y <- Y E and Z <- E Z of a Newton-DB iteration, launched
+// together; a type of its own so that profiles list this launch separately.
+struct EpiPair : EpiStore {};
+
 // Output through a block descriptor: only rows x cols of the block is written.
 struct EpiStoreDesc {
   static constexpr bool kReduce = false;

@@ -24,6 +24,28 @@ int tile_of(int B) { return (B % 128 == 0) ? 128 : 64; }
 
 int check_launch() { return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMPOO_EHIP; }
 
+// Timing hook (shampoo_timing_hook): events recorded around launches of one
+// kernel family on the launch's own stream.
+struct TimingHook {
+  int family = 0;
+  hipEvent_t* events = nullptr;
+  int capacity = 0;
+  int count = 0;
+} g_timing;
+
+bool timing_on(int fam) {
+  return fam != 0 && g_timing.family == fam && g_timing.count < g_timing.capacity;
+}
+void timing_before(int fam, hipStream_t st) {
+  if (timing_on(fam)) hipEventRecord(g_timing.events[2 * g_timing.count], st);
+}
+void timing_after(int fam, hipStream_t st) {
+  if (timing_on(fam)) {
+    hipEventRecord(g_timing.events[2 * g_timing.count + 1], st);
+    ++g_timing.count;
+  }
+}
+
 // Sequential carving of a workspace; `base == nullptr` only measures.
 struct Carver {
   char* base;
@@ -57,7 +79,7 @@ int gemm_tiles(int B) {
 // ---------------------------------------------------------------------------
 template <int LA, int LB, bool DA, bool DB, class Epi>
 int run_gemm(const Operand* a, const Operand* b, const typename Epi::Job* e, int njobs, int64_t nitems,
-             int B, bool sym, hipStream_t st) {
+             int B, bool sym, hipStream_t st, int fam = 0) {
   GemmLaunch<Epi> P;
   memset(&P, 0, sizeof(P));
   for (int j = 0; j < njobs; ++j) {
@@ -75,10 +97,12 @@ int run_gemm(const Operand* a, const Operand* b, const typename Epi::Job* e, int
   if (total == 0) return SHAMPOO_OK;
   if (total > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
   P.total = (uint32_t)total;
+  timing_before(fam, st);
   if (T == 128)
     hipLaunchKernelGGL((gemm_f32_kernel<2, 2, LA, LB, DA, DB, Epi>), dim3(P.total), dim3(kGemmThreads), 0, st, P);
   else
     hipLaunchKernelGGL((gemm_f32_kernel<1, 1, LA, LB, DA, DB, Epi>), dim3(P.total), dim3(kGemmThreads), 0, st, P);
+  timing_after(fam, st);
   return check_launch();
 }
 
@@ -88,13 +112,13 @@ Operand blocks(const shampoo_block* d) { return Operand{nullptr, d}; }
 // Plain product of two dense stacks, C = A B, with the given epilogue.
 template <class Epi>
 int gemm_nn(const float* const* A, const float* const* Bm, const typename Epi::Job* e, int njobs, int64_t n,
-            int B, hipStream_t st) {
+            int B, hipStream_t st, int fam = 0) {
   Operand oa[2], ob[2];
   for (int j = 0; j < njobs; ++j) {
     oa[j] = dense(A[j]);
     ob[j] = dense(Bm[j]);
   }
-  return run_gemm<KCONTIG, MNCONTIG, false, false, Epi>(oa, ob, e, njobs, n, B, false, st);
+  return run_gemm<KCONTIG, MNCONTIG, false, false, Epi>(oa, ob, e, njobs, n, B, false, st, fam);
 }
 
 template <int MODE>
@@ -390,7 +414,7 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
       j.tiles = tiles;
       const float* A[1] = {Z};
       const float* Bm[1] = {Y};
-      SHP_TRY(gemm_nn<EpiNdbE>(A, Bm, &j, 1, nf, B, c.st));
+      SHP_TRY(gemm_nn<EpiNdbE>(A, Bm, &j, 1, nf, B, c.st, SHAMPOO_TIME_NDB_P));
       SHP_TRY(run_resid(c.ws->partials, tiles, c.resid, c.ncols, pass * c.iters + it, c.status, nf, c.st));
     }
     const bool last = (it == c.iters - 1);
@@ -399,10 +423,10 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
       if (Yn == nullptr) return SHAMPOO_EWORKSPACE;
       float* Zn = pool.get();
       if (Zn == nullptr) return SHAMPOO_EWORKSPACE;
-      EpiStore::Job j[2] = {plain_job(Yn), plain_job(Zn)};
+      EpiPair::Job j[2] = {plain_job(Yn), plain_job(Zn)};
       const float* A[2] = {Y, En};
       const float* Bm[2] = {En, Z};
-      SHP_TRY(gemm_nn<EpiStore>(A, Bm, j, 2, nf, B, c.st));
+      SHP_TRY(gemm_nn<EpiPair>(A, Bm, j, 2, nf, B, c.st, SHAMPOO_TIME_NDB_PAIR));
       pool.put(Y);
       pool.put(Z);
       pool.put(En);
@@ -629,12 +653,15 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
     e.status = status;
     e.pexp = pexp;
     if (bf) {
-      SHP_TRY(bf16_gemm_nt_clenshaw(ws->b16[s1], ws->as_t16, e, nf, B, st));
+      timing_before(SHAMPOO_TIME_CLENSHAW, st);
+      const int rc = bf16_gemm_nt_clenshaw(ws->b16[s1], ws->as_t16, e, nf, B, st);
+      timing_after(SHAMPOO_TIME_CLENSHAW, st);
+      SHP_TRY(rc);
       s1 ^= 1;
     } else {
       const float* A[1] = {ws->as};
       const float* Bm[1] = {ws->b[i1]};
-      SHP_TRY(gemm_nn<EpiClenshaw>(A, Bm, &e, 1, nf, B, st));
+      SHP_TRY(gemm_nn<EpiClenshaw>(A, Bm, &e, 1, nf, B, st, SHAMPOO_TIME_CLENSHAW));
     }
     const int t = i2;
     i2 = i1;
@@ -652,6 +679,18 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
 extern "C" {
 
 int shampoo_abi_version(void) { return SHAMPOO_ABI_VERSION; }
+
+int shampoo_timing_hook(int family, hipEvent_t* events, int capacity) {
+  if (family < 0 || family > SHAMPOO_TIME_CLENSHAW || capacity < 0) return SHAMPOO_EINVAL;
+  if (family != 0 && (events == nullptr || capacity == 0)) return SHAMPOO_EINVAL;
+  g_timing.family = family;
+  g_timing.events = family ? events : nullptr;
+  g_timing.capacity = family ? capacity : 0;
+  g_timing.count = 0;
+  return SHAMPOO_OK;
+}
+
+int shampoo_timing_count(void) { return g_timing.count; }
 
 const char* shampoo_strerror(int code) {
   switch (code) {
