@@ -84,6 +84,15 @@ enum {
   SHAMPOO_CN = 2              /* coupled Newton */
 };
 
+/* Modifier bit, OR-ed into `variant` (shampoo_invroot_newton) or `prec`
+ * (shampoo_invroot_cheby).  By default every product whose result is a
+ * polynomial in the factor -- Newton-DB's Y E and E Z, coupled Newton's X C
+ * and powers of C, Clenshaw's A_s b -- is symmetric in exact arithmetic, so
+ * only its upper-triangular tiles are computed and mirrored (the outputs are
+ * exactly symmetric).  The coupling products Z Y and C^p M are always full.
+ * With this bit set every product is computed in full. */
+#define SHAMPOO_FULL_PRODUCTS 0x100
+
 /* Operation ids of shampoo_workspace_bytes. */
 enum {
   SHAMPOO_OP_ACCUMULATE = 1,

@@ -35,6 +35,8 @@ SCALE_FROBENIUS = 1
 NDB = 0
 NDB_Z = 1
 CN = 2
+# Modifier bit for variant (newton) / prec (cheby): compute symmetric products in full
+FULL_PRODUCTS = 0x100
 # Workspace op ids
 OP_ACCUMULATE = 1
 OP_SCALE = 2

@@ -16,6 +16,7 @@ constexpr int kBK16 = 64;
 constexpr int kLd16 = kBK16 + 8;  // LDS row stride in bf16 elements (144 bytes)
 
 struct EpiStoreBf16 {
+  static constexpr bool kSym = false;
   static constexpr bool kReduce = false;
   struct Job {
     uint16_t* out;
@@ -140,8 +141,13 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<E
   }
 
   typename Epi::Tile tile(P.e, item, P.B);
-  const bool diag_tile = P.sym && tm == tn;
-  const bool mirror = P.sym && tm != tn;
+  if constexpr (Epi::kSym) {
+    static_assert(sizeof(lds) >= sizeof(float) * BM * (BN + 1), "LDS too small for the transpose");
+    if (P.sym) {
+      sym_epilogue<TM, TN>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, lane, tm == tn);
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -150,16 +156,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<E
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
         const int col = n0 + wn + 32 * j + rr;
-        const float v = acc[i][j][e];
-        if (diag_tile) {
-          if (row <= col) {
-            tile.store(row, col, v);
-            if (row != col) tile.store(col, row, v);
-          }
-        } else {
-          tile.store(row, col, v);
-          if (mirror) tile.store(col, row, v);
-        }
+        tile.store(row, col, acc[i][j][e]);
       }
 }
 
@@ -279,8 +276,8 @@ static inline int bf16_gemm_nt_store(const uint16_t* a, const uint16_t* bt, cons
 }
 
 static inline int bf16_gemm_nt_clenshaw(const uint16_t* a, const uint16_t* bt, const EpiClenshaw::Job& e,
-                                        int64_t n, int B, hipStream_t st) {
-  return bf16_gemm_nt<EpiClenshaw>(a, bt, e, n, B, false, st);
+                                        int64_t n, int B, bool sym, hipStream_t st) {
+  return bf16_gemm_nt<EpiClenshaw>(a, bt, e, n, B, sym, st);
 }
 
 static inline int bf16_gemm_nt_bf16out(const uint16_t* a, const uint16_t* bt, uint16_t* out, int64_t n, int B,

@@ -142,6 +142,40 @@ struct GemmLaunch {
   uint32_t total;      // njobs * nitems * tiles_per_item
 };
 
+// Epilogue of a symmetric product (only tiles with tm <= tn are computed).
+// Each lane forms its outputs o = tile.value(...) at their own positions;
+// an off-diagonal tile writes them there and, through an LDS transpose,
+// coalesced at the mirrored positions; a diagonal tile writes its upper
+// triangle and mirrors it into the lower one.  `lds` must hold
+// 64 TM x (64 TN + 1) floats and be free (the main loop has ended with a
+// barrier).  The accumulator layout is that of the 32 x 32 MFMA blocks.
+template <int TM, int TN, class Tile>
+__device__ __forceinline__ void sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN], float* lds, int m0, int n0,
+                                             int wm, int wn, int lane, bool diag) {
+  constexpr int BM = 64 * TM, BN = 64 * TN, LD = BN + 1;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rl = wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int cl = wn + 32 * j + (lane & 31);
+        const float o = tile.value(m0 + rl, n0 + cl, acc[i][j][e]);
+        if (!diag) tile.write(m0 + rl, n0 + cl, o);
+        lds[rl * LD + cl] = o;
+      }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < BM * BN; idx += kGemmThreads) {
+    const int a = idx / BM, b = idx - (idx / BM) * BM;
+    if (!diag) {
+      tile.write(n0 + a, m0 + b, lds[b * LD + a]);  // (n0 + a, m0 + b) mirrors (m0 + b, n0 + a)
+    } else {
+      tile.write(m0 + a, m0 + b, (a <= b) ? lds[a * LD + b] : lds[b * LD + a]);
+    }
+  }
+}
+
 template <int TM, int TN, int LA, int LB, bool DA, bool DB, class Epi>
 __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLaunch<Epi> P) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
@@ -233,8 +267,13 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLau
   // Epilogue.  Accumulator e of block (i, j) sits at
   // row = 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = 32 j + lane % 32.
   typename Epi::Tile tile(P.e[job], item, P.B);
-  const bool diag_tile = P.sym && tm == tn;
-  const bool mirror = P.sym && tm != tn;
+  if constexpr (Epi::kSym) {
+    static_assert(2 * (SA::kFloats + SB::kFloats) >= BM * (BN + 1), "LDS too small for the transpose");
+    if (P.sym) {
+      sym_epilogue<TM, TN>(tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
+      return;
+    }
+  }
   float part = 0.f;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -244,16 +283,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLau
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         const int col = n0 + wn + 32 * j + (lane & 31);
-        const float v = acc[i][j][e];
-        if (diag_tile) {
-          if (row <= col) {
-            part += tile.store(row, col, v);
-            if (row != col) tile.store(col, row, v);
-          }
-        } else {
-          part += tile.store(row, col, v);
-          if (mirror) tile.store(col, row, v);
-        }
+        part += tile.store(row, col, acc[i][j][e]);
       }
   if (Epi::kReduce) {
     const float tot = block_sum<kGemmThreads>(part, red);
@@ -265,6 +295,10 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLau
 // Epilogues.  Tile(job, item, B) is built once per workgroup; store(row, col,
 // v) writes the output for one accumulator and returns its contribution to
 // the tile's reduction (if any); partial(t, sum) stores that reduction.
+// Epilogues with kSym also split store into value(row, col, v) -> o and
+// write(row, col, o) for symmetric products; there the output at a mirrored
+// position is the value formed at the computed one, which assumes the other
+// inputs of the epilogue (an EMA state, Clenshaw terms) are symmetric too.
 // ---------------------------------------------------------------------------
 
 // out = mult * acc + beta * cin (cin may alias out); X = I for a degenerate
@@ -272,6 +306,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLau
 // `scale` is given, else alpha.
 struct EpiStore {
   static constexpr bool kReduce = false;
+  static constexpr bool kSym = true;
   struct Job {
     float* out;
     const float* cin;
@@ -295,12 +330,15 @@ struct EpiStore {
       if (j.scale) mult *= j.extra * powf(safe_c(j.scale, j.status, item), j.pexp);
       ident = j.status && degenerate(j.status[item]);
     }
-    __device__ __forceinline__ float store(int row, int col, float v) {
-      const int64_t idx = (int64_t)row * B + col;
+    __device__ __forceinline__ float value(int row, int col, float v) const {
       float o = mult * v;
-      if (cin) o += beta * cin[idx];
+      if (cin) o += beta * cin[(int64_t)row * B + col];
       if (ident) o = (row == col) ? 1.f : 0.f;
-      out[idx] = o;
+      return o;
+    }
+    __device__ __forceinline__ void write(int row, int col, float o) { out[(int64_t)row * B + col] = o; }
+    __device__ __forceinline__ float store(int row, int col, float v) {
+      write(row, col, value(row, col, v));
       return 0.f;
     }
     __device__ void partial(int, float) {}
@@ -313,6 +351,7 @@ struct EpiPair : EpiStore {};
 
 // Output through a block descriptor: only rows x cols of the block is written.
 struct EpiStoreDesc {
+  static constexpr bool kSym = false;
   static constexpr bool kReduce = false;
   struct Job {
     const shampoo_block* out;
@@ -340,6 +379,7 @@ struct EpiStoreDesc {
 
 // Newton-DB: P = Z Y -> E = (3 I - P) / 2, reduction ||I - P||_F^2.
 struct EpiNdbE {
+  static constexpr bool kSym = false;
   static constexpr bool kReduce = true;
   struct Job {
     float* e;
@@ -367,6 +407,7 @@ struct EpiNdbE {
 // Coupled Newton: M' = C^p M -> store M' and C' = ((p+1) I - M') / p,
 // reduction ||I - M'||_F^2.
 struct EpiCnM {
+  static constexpr bool kSym = false;
   static constexpr bool kReduce = true;
   struct Job {
     float* m;
@@ -407,6 +448,7 @@ struct EpiCnM {
 // An optional bf16 copy of b is written for the next bf16 product.
 struct EpiClenshaw {
   static constexpr bool kReduce = false;
+  static constexpr bool kSym = true;
   struct Job {
     float* out;
     uint16_t* out_bf16;
@@ -445,13 +487,20 @@ struct EpiClenshaw {
         ident = false;
       }
     }
-    __device__ __forceinline__ float store(int row, int col, float v) {
+    __device__ __forceinline__ float value(int row, int col, float v) const {
       const int64_t idx = (int64_t)row * B + col;
       const float d = (row == col) ? cj : 0.f;
       float o = mult * (d + k1 * v - k2 * b1[idx] - b2[idx]);
       if (ident) o = (row == col) ? 1.f : 0.f;
+      return o;
+    }
+    __device__ __forceinline__ void write(int row, int col, float o) {
+      const int64_t idx = (int64_t)row * B + col;
       out[idx] = o;
       if (obf) obf[idx] = f32_to_bf16_bits(o);
+    }
+    __device__ __forceinline__ float store(int row, int col, float v) {
+      write(row, col, value(row, col, v));
       return 0.f;
     }
     __device__ void partial(int, float) {}

@@ -37,11 +37,11 @@ bool timing_on(int fam) {
   return fam != 0 && g_timing.family == fam && g_timing.count < g_timing.capacity;
 }
 void timing_before(int fam, hipStream_t st) {
-  if (timing_on(fam)) hipEventRecord(g_timing.events[2 * g_timing.count], st);
+  if (timing_on(fam)) (void)hipEventRecord(g_timing.events[2 * g_timing.count], st);
 }
 void timing_after(int fam, hipStream_t st) {
   if (timing_on(fam)) {
-    hipEventRecord(g_timing.events[2 * g_timing.count + 1], st);
+    (void)hipEventRecord(g_timing.events[2 * g_timing.count + 1], st);
     ++g_timing.count;
   }
 }
@@ -110,15 +110,17 @@ Operand dense(const float* p) { return Operand{p, nullptr}; }
 Operand blocks(const shampoo_block* d) { return Operand{nullptr, d}; }
 
 // Plain product of two dense stacks, C = A B, with the given epilogue.
+// With `sym`, the product is known to be symmetric (in exact arithmetic):
+// only the upper-triangular tiles are computed and mirrored.
 template <class Epi>
 int gemm_nn(const float* const* A, const float* const* Bm, const typename Epi::Job* e, int njobs, int64_t n,
-            int B, hipStream_t st, int fam = 0) {
+            int B, hipStream_t st, bool sym = false, int fam = 0) {
   Operand oa[2], ob[2];
   for (int j = 0; j < njobs; ++j) {
     oa[j] = dense(A[j]);
     ob[j] = dense(Bm[j]);
   }
-  return run_gemm<KCONTIG, MNCONTIG, false, false, Epi>(oa, ob, e, njobs, n, B, false, st, fam);
+  return run_gemm<KCONTIG, MNCONTIG, false, false, Epi>(oa, ob, e, njobs, n, B, sym, st, fam);
 }
 
 template <int MODE>
@@ -312,6 +314,7 @@ struct NdbCtx {
   int32_t* status;
   NewtonWs* ws;
   hipStream_t st;
+  bool sym;  // the updates Y E and E Z are symmetric: upper tiles only
 };
 
 // One Newton-DB pass.  The prologue reads `src` and forms Y0 = a src + b I
@@ -357,7 +360,7 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
         EpiStore::Job j = final_job(fo);
         const float* A[1] = {Y};
         const float* Bm[1] = {E};
-        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st));
+        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st, c.sym));
         *result = nullptr;
       } else {
         float* Yn = pool.get();
@@ -365,7 +368,7 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
         EpiStore::Job j = plain_job(Yn);
         const float* A[1] = {Y};
         const float* Bm[1] = {E};
-        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st));
+        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st, c.sym));
         *result = Yn;
       }
       pool.put(Y);
@@ -399,7 +402,7 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
     EpiStore::Job j = plain_job(Yn);
     const float* A[1] = {Y};
     const float* Bm[1] = {E};
-    SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st));
+    SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st, c.sym));
     pool.put(Y);
     Y = Yn;
   }
@@ -414,7 +417,7 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
       j.tiles = tiles;
       const float* A[1] = {Z};
       const float* Bm[1] = {Y};
-      SHP_TRY(gemm_nn<EpiNdbE>(A, Bm, &j, 1, nf, B, c.st, SHAMPOO_TIME_NDB_P));
+      SHP_TRY(gemm_nn<EpiNdbE>(A, Bm, &j, 1, nf, B, c.st, false, SHAMPOO_TIME_NDB_P));
       SHP_TRY(run_resid(c.ws->partials, tiles, c.resid, c.ncols, pass * c.iters + it, c.status, nf, c.st));
     }
     const bool last = (it == c.iters - 1);
@@ -426,7 +429,7 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
       EpiPair::Job j[2] = {plain_job(Yn), plain_job(Zn)};
       const float* A[2] = {Y, En};
       const float* Bm[2] = {En, Z};
-      SHP_TRY(gemm_nn<EpiPair>(A, Bm, j, 2, nf, B, c.st, SHAMPOO_TIME_NDB_PAIR));
+      SHP_TRY(gemm_nn<EpiPair>(A, Bm, j, 2, nf, B, c.st, c.sym, SHAMPOO_TIME_NDB_PAIR));
       pool.put(Y);
       pool.put(Z);
       pool.put(En);
@@ -438,7 +441,7 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
       EpiStore::Job j = fo.x ? final_job(fo) : plain_job(dst);
       const float* A[1] = {want_y ? Y : En};
       const float* Bm[1] = {want_y ? En : Z};
-      SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st));
+      SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, c.st, c.sym));
       pool.put(Y);
       pool.put(Z);
       pool.put(En);
@@ -449,8 +452,8 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
 }
 
 int newton_db(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, bool zchain, int iters,
-              float* x, float* resid, int32_t* status, NewtonWs* ws, hipStream_t st) {
-  NdbCtx c{nf, B, iters, resid, (p == 2 ? 1 : 2) * iters, status, ws, st};
+              float* x, float* resid, int32_t* status, NewtonWs* ws, hipStream_t st, bool sym) {
+  NdbCtx c{nf, B, iters, resid, (p == 2 ? 1 : 2) * iters, status, ws, st, sym};
   FinalOut fo{x, sc, status, -1.f / (float)p, 1.f};
   float* r1 = nullptr;
   if (p == 2) return ndb_pass(c, F, false, sc, 0.f, 0.f, false, 0, fo, &r1);
@@ -471,7 +474,7 @@ int newton_db(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
 // Coupled Newton.
 // ---------------------------------------------------------------------------
 int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, int iters, float* x,
-                   float* resid, int32_t* status, NewtonWs* ws, hipStream_t st) {
+                   float* resid, int32_t* status, NewtonWs* ws, hipStream_t st, bool sym) {
   Pool& pool = ws->pool;
   float* M = pool.get();
   if (M == nullptr) return SHAMPOO_EWORKSPACE;
@@ -514,7 +517,7 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
       EpiStore::Job j = final_job(fo);
       const float* A[1] = {X};
       const float* Bm[1] = {C};
-      return gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st);
+      return gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st, sym);
     }
     // C^p by squaring, with X C in the same launch as the first square.
     float* Cp = C;
@@ -531,12 +534,12 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
         EpiStore::Job j[2] = {plain_job(Xn), plain_job(C2)};
         const float* A[2] = {X, C};
         const float* Bm[2] = {C, C};
-        SHP_TRY(gemm_nn<EpiStore>(A, Bm, j, 2, nf, B, st));
+        SHP_TRY(gemm_nn<EpiStore>(A, Bm, j, 2, nf, B, st, sym));
       } else {
         EpiStore::Job j = plain_job(C2);
         const float* A[1] = {C};
         const float* Bm[1] = {C};
-        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st));
+        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st, sym));
       }
       Cp = C2;
       for (int q = 4; q <= p; q *= 2) {
@@ -545,7 +548,7 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
         EpiStore::Job j = plain_job(Cq);
         const float* A[1] = {Cp};
         const float* Bm[1] = {Cp};
-        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st));
+        SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st, sym));
         pool.put(Cp);
         Cp = Cq;
       }
@@ -555,7 +558,7 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
       EpiStore::Job j = plain_job(Xn);
       const float* A[1] = {X};
       const float* Bm[1] = {C};
-      SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st));
+      SHP_TRY(gemm_nn<EpiStore>(A, Bm, &j, 1, nf, B, st, sym));
     }
     // M_{k+1} = C^p M_k, C_{k+1} = ((p+1) I - M_{k+1}) / p.
     float* Mn = pool.get();
@@ -608,7 +611,7 @@ void cheby_fit(int degree, int p, double delta, double* c) {
 }
 
 int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, int degree, double delta,
-              int prec, float* x, int32_t* status, ChebyWs* ws, hipStream_t st) {
+              int prec, float* x, int32_t* status, ChebyWs* ws, hipStream_t st, bool sym) {
   double c[257];
   cheby_fit(degree, p, delta, c);
   const float pexp = -1.f / (float)p;
@@ -654,14 +657,14 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
     e.pexp = pexp;
     if (bf) {
       timing_before(SHAMPOO_TIME_CLENSHAW, st);
-      const int rc = bf16_gemm_nt_clenshaw(ws->b16[s1], ws->as_t16, e, nf, B, st);
+      const int rc = bf16_gemm_nt_clenshaw(ws->b16[s1], ws->as_t16, e, nf, B, sym, st);
       timing_after(SHAMPOO_TIME_CLENSHAW, st);
       SHP_TRY(rc);
       s1 ^= 1;
     } else {
       const float* A[1] = {ws->as};
       const float* Bm[1] = {ws->b[i1]};
-      SHP_TRY(gemm_nn<EpiClenshaw>(A, Bm, &e, 1, nf, B, st, SHAMPOO_TIME_CLENSHAW));
+      SHP_TRY(gemm_nn<EpiClenshaw>(A, Bm, &e, 1, nf, B, st, sym, SHAMPOO_TIME_CLENSHAW));
     }
     const int t = i2;
     i2 = i1;
@@ -704,6 +707,8 @@ const char* shampoo_strerror(int code) {
 }
 
 size_t shampoo_workspace_bytes(int op, int64_t count, int B, int variant_or_degree, int prec) {
+  prec &= ~SHAMPOO_FULL_PRODUCTS;
+  if (op == SHAMPOO_OP_NEWTON) variant_or_degree &= ~SHAMPOO_FULL_PRODUCTS;
   if (count < 0 || !valid_B(B)) return 0;
   if (prec != SHAMPOO_F32 && prec != SHAMPOO_BF16_IN) return 0;
   Carver c(nullptr);
@@ -823,6 +828,8 @@ int shampoo_scale_power(const float* factors, int64_t nfactors, int B, float eps
 int shampoo_invroot_newton(const float* factors, const shampoo_scale* scale, int64_t nfactors, int B, int p,
                            int variant, int iters, float* x_out, float* resid_out, int32_t* status, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
+  const bool sym = (variant & SHAMPOO_FULL_PRODUCTS) == 0;
+  variant &= ~SHAMPOO_FULL_PRODUCTS;
   if (nfactors < 0) return SHAMPOO_EINVAL;
   if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
   if (variant < SHAMPOO_NDB || variant > SHAMPOO_CN) return SHAMPOO_EINVAL;
@@ -841,14 +848,16 @@ int shampoo_invroot_newton(const float* factors, const shampoo_scale* scale, int
   NewtonWs w;
   newton_layout(c, nfactors, B, variant, &w);
   if (variant == SHAMPOO_CN)
-    return coupled_newton(factors, scale, nfactors, B, p, iters, x_out, resid_out, status, &w, stream);
+    return coupled_newton(factors, scale, nfactors, B, p, iters, x_out, resid_out, status, &w, stream, sym);
   return newton_db(factors, scale, nfactors, B, p, variant == SHAMPOO_NDB_Z, iters, x_out, resid_out, status, &w,
-                   stream);
+                   stream, sym);
 }
 
 int shampoo_invroot_cheby(const float* factors, const shampoo_scale* scale, int64_t nfactors, int B, int p,
                           int degree, double interval_eps, int prec, float* x_out, int32_t* status, void* ws,
                           size_t ws_bytes, hipStream_t stream) {
+  const bool sym = (prec & SHAMPOO_FULL_PRODUCTS) == 0;
+  prec &= ~SHAMPOO_FULL_PRODUCTS;
   if (nfactors < 0) return SHAMPOO_EINVAL;
   if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
   if (p < 1 || p > 64) return SHAMPOO_EINVAL;
@@ -864,7 +873,7 @@ int shampoo_invroot_cheby(const float* factors, const shampoo_scale* scale, int6
   Carver c(ws);
   ChebyWs w;
   cheby_layout(c, nfactors, B, prec, &w);
-  return chebyshev(factors, scale, nfactors, B, p, degree, interval_eps, prec, x_out, status, &w, stream);
+  return chebyshev(factors, scale, nfactors, B, p, degree, interval_eps, prec, x_out, status, &w, stream, sym);
 }
 
 int shampoo_precondition(const float* x_roots, const shampoo_block* g_blocks, int64_t nblocks, int B,

@@ -141,15 +141,17 @@ NEWTON_CASES = [
 ]
 
 
+@pytest.mark.parametrize("full", [False, True])
 @pytest.mark.parametrize("B", [64, 256])
 @pytest.mark.parametrize("variant,p,iters", NEWTON_CASES)
-def test_newton_matches_oracle(B, variant, p, iters):
+def test_newton_matches_oracle(B, variant, p, iters, full):
     nf = 4
     F = W.spd_factors(30 + B, nf, B, cond=1e3)
     V0 = W.start_vectors(31, nf, B)
     Fd = dev(F)
     sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
-    X, R = gpu_roots(Fd, sc, st, "newton", iters=iters, p=p, variant=variant, resid=True)
+    v = variant | (capi.FULL_PRODUCTS if full else 0)
+    X, R = gpu_roots(Fd, sc, st, "newton", iters=iters, p=p, variant=v, resid=True)
     Xh, Rh = host(X), host(R)
     err = 0.0
     for i in range(nf):
@@ -158,7 +160,10 @@ def test_newton_matches_oracle(B, variant, p, iters):
         err = max(err, O.relative_frobenius(Xh[i], ref))
     assert err <= TOL_F32, err
     assert np.all(Rh >= 0.0) and np.all(np.isfinite(Rh))
-    report("newton", B=B, variant=variant, p=p, iters=iters, err=err)
+    if not full and not (variant == capi.CN and iters > 1):
+        # products of commuting polynomials are formed from upper tiles: exactly symmetric
+        assert all(np.array_equal(Xh[i], Xh[i].T) for i in range(nf))
+    report("newton", B=B, variant=variant, p=p, iters=iters, full=full, err=err)
 
 
 def test_newton_db_residuals_match_oracle():
@@ -176,39 +181,44 @@ def test_newton_db_residuals_match_oracle():
         assert np.allclose(Rh[i], res, rtol=1e-3, atol=1e-5), (Rh[i], res)
 
 
+@pytest.mark.parametrize("full", [False, True])
 @pytest.mark.parametrize("B", [64, 128])
 @pytest.mark.parametrize("degree", [1, 2, 3, 16, 32])
-def test_chebyshev_f32_matches_oracle(B, degree):
+def test_chebyshev_f32_matches_oracle(B, degree, full):
     nf = 4
     F = W.spd_factors(50 + B, nf, B, cond=1e4)
     V0 = W.start_vectors(51, nf, B)
     Fd = dev(F)
     sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
-    X, _ = gpu_roots(Fd, sc, st, "cheby", degree=degree)
+    X, _ = gpu_roots(Fd, sc, st, "cheby", degree=degree, prec=capi.F32 | (capi.FULL_PRODUCTS if full else 0))
     Xh = host(X)
     err = 0.0
     for i in range(nf):
         o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
         err = max(err, O.relative_frobenius(Xh[i], oracle_root(F[i], o, "cheby", degree=degree)))
     assert err <= TOL_F32, err
-    report("cheby_f32", B=B, degree=degree, err=err)
+    if not full:
+        assert all(np.array_equal(Xh[i], Xh[i].T) for i in range(nf))
+    report("cheby_f32", B=B, degree=degree, full=full, err=err)
 
 
+@pytest.mark.parametrize("full", [False, True])
 @pytest.mark.parametrize("degree", [2, 16, 24])
-def test_chebyshev_bf16_matches_oracle(degree):
+def test_chebyshev_bf16_matches_oracle(degree, full):
     nf, B = 4, 256
     F = W.spd_factors(60, nf, B, cond=1e4)
     V0 = W.start_vectors(61, nf, B)
     Fd = dev(F)
     sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
-    X, _ = gpu_roots(Fd, sc, st, "cheby", degree=degree, prec=capi.BF16_IN)
+    X, _ = gpu_roots(Fd, sc, st, "cheby", degree=degree,
+                     prec=capi.BF16_IN | (capi.FULL_PRODUCTS if full else 0))
     Xh = host(X)
     err = 0.0
     for i in range(nf):
         o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
         err = max(err, O.relative_frobenius(Xh[i], oracle_root(F[i], o, "cheby", degree=degree)))
     assert err <= TOL_BF16, err
-    report("cheby_bf16", degree=degree, err=err)
+    report("cheby_bf16", degree=degree, full=full, err=err)
 
 
 # ---------------------------------------------------------------------------
