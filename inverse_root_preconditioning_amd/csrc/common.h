@@ -11,6 +11,8 @@ namespace shp {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
@@ -22,6 +24,20 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t hw, uint32_t total) {
   const uint32_t q = total / kXcds, r = total % kXcds;
   const uint32_t xcd = hw % kXcds, local = hw / kXcds;
   return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+// Global-memory access through an explicit global address space.  Pointers
+// that the compiler cannot trace to a kernel argument (descriptor tables,
+// pointers picked at run time) would otherwise become flat accesses, which
+// also count against the LDS wait counter and so serialise LDS waits with
+// outstanding global loads.
+template <class T>
+__device__ __forceinline__ T ldg(const T* p) {
+  return *(const __attribute__((address_space(1))) T*)p;
+}
+template <class T>
+__device__ __forceinline__ void stg(T* p, const T& v) {
+  *(__attribute__((address_space(1))) T*)p = v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

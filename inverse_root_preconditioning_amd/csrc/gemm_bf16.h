@@ -26,7 +26,7 @@ struct EpiStoreBf16 {
     int B;
     __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) { out = j.out + item * (int64_t)B_ * B_; }
     __device__ __forceinline__ float store(int row, int col, float v) {
-      out[(int64_t)row * B + col] = f32_to_bf16_bits(v);
+      stg(out + (int64_t)row * B + col, f32_to_bf16_bits(v));
       return 0.f;
     }
     __device__ void partial(int, float) {}
@@ -46,7 +46,7 @@ struct Bf16Launch {
   uint32_t total;
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) {
   bf16x8 r;
   __builtin_memcpy(&r, &u, sizeof(r));
   return r;
@@ -93,14 +93,14 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<E
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  uint4 ra[4], rb[4];
+  u32x4 ra[4], rb[4];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int idx = tid + 256 * it;
       const int row = idx >> 3, ch = idx & 7;
-      ra[it] = *reinterpret_cast<const uint4*>(A + (int64_t)(m0 + row) * P.B + k0 + ch * 8);
-      rb[it] = *reinterpret_cast<const uint4*>(Bt + (int64_t)(n0 + row) * P.B + k0 + ch * 8);
+      ra[it] = ldg(reinterpret_cast<const u32x4*>(A + (int64_t)(m0 + row) * P.B + k0 + ch * 8));
+      rb[it] = ldg(reinterpret_cast<const u32x4*>(Bt + (int64_t)(n0 + row) * P.B + k0 + ch * 8));
     }
   };
   auto sstore = [&](uint16_t* buf) {
@@ -108,8 +108,8 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<E
     for (int it = 0; it < 4; ++it) {
       const int idx = tid + 256 * it;
       const int row = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<uint4*>(buf + row * kLd16 + ch * 8) = ra[it];
-      *reinterpret_cast<uint4*>(buf + kTile + row * kLd16 + ch * 8) = rb[it];
+      *reinterpret_cast<u32x4*>(buf + row * kLd16 + ch * 8) = ra[it];
+      *reinterpret_cast<u32x4*>(buf + kTile + row * kLd16 + ch * 8) = rb[it];
     }
   };
 
@@ -125,11 +125,11 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<E
       bf16x8 fa[TM], fb[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        fa[i] = as_bf16x8(*reinterpret_cast<const uint4*>(cur + (wm + 32 * i + rr) * kLd16 + ks * 16 + h * 8));
+        fa[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(cur + (wm + 32 * i + rr) * kLd16 + ks * 16 + h * 8));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         fb[j] = as_bf16x8(
-            *reinterpret_cast<const uint4*>(cur + kTile + (wn + 32 * j + rr) * kLd16 + ks * 16 + h * 8));
+            *reinterpret_cast<const u32x4*>(cur + kTile + (wn + 32 * j + rr) * kLd16 + ks * 16 + h * 8));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -188,11 +188,11 @@ __global__ void __launch_bounds__(256) bf16_cast_kernel(const CastArgs P) {
     if (row < v.rows) {
       const float* src = v.p + (int64_t)row * v.ld + col;
       if (v.vec && col + 3 < v.cols) {
-        x = *reinterpret_cast<const floatx4*>(src);
+        x = ldg(reinterpret_cast<const floatx4*>(src));
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (col + e < v.cols) x[e] = src[e];
+          if (col + e < v.cols) x[e] = ldg(src + e);
       }
     }
 #pragma unroll
@@ -204,16 +204,16 @@ __global__ void __launch_bounds__(256) bf16_cast_kernel(const CastArgs P) {
   for (int i = 0; i < 4; ++i) {
     const int lr = cr + 16 * i;
     if (P.out) {
-      uint2 w;
+      u32x2 w;
       w.x = (uint32_t)f32_to_bf16_bits(t[lr][cc]) | ((uint32_t)f32_to_bf16_bits(t[lr][cc + 1]) << 16);
       w.y = (uint32_t)f32_to_bf16_bits(t[lr][cc + 2]) | ((uint32_t)f32_to_bf16_bits(t[lr][cc + 3]) << 16);
-      *reinterpret_cast<uint2*>(P.out + base + (int64_t)(r0 + lr) * P.B + c0 + cc) = w;
+      stg(reinterpret_cast<u32x2*>(P.out + base + (int64_t)(r0 + lr) * P.B + c0 + cc), w);
     }
     if (P.out_t) {
-      uint2 w;
+      u32x2 w;
       w.x = (uint32_t)f32_to_bf16_bits(t[cc][lr]) | ((uint32_t)f32_to_bf16_bits(t[cc + 1][lr]) << 16);
       w.y = (uint32_t)f32_to_bf16_bits(t[cc + 2][lr]) | ((uint32_t)f32_to_bf16_bits(t[cc + 3][lr]) << 16);
-      *reinterpret_cast<uint2*>(P.out_t + base + (int64_t)(c0 + lr) * P.B + r0 + cc) = w;
+      stg(reinterpret_cast<u32x2*>(P.out_t + base + (int64_t)(c0 + lr) * P.B + r0 + cc), w);
     }
   }
 }

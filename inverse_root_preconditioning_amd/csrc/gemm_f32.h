@@ -82,17 +82,17 @@ struct Stager {
         scol = mn0 + (idx % (MN / 4)) * 4;
       }
       if (!DESC) {
-        r[it] = *reinterpret_cast<const floatx4*>(v.p + (int64_t)srow * v.ld + scol);
+        r[it] = ldg(reinterpret_cast<const floatx4*>(v.p + (int64_t)srow * v.ld + scol));
       } else {
         floatx4 x = {0.f, 0.f, 0.f, 0.f};
         if (srow < v.rows) {
           const float* src = v.p + (int64_t)srow * v.ld + scol;
           if (v.vec && scol + 3 < v.cols) {
-            x = *reinterpret_cast<const floatx4*>(src);
+            x = ldg(reinterpret_cast<const floatx4*>(src));
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (scol + e < v.cols) x[e] = src[e];
+              if (scol + e < v.cols) x[e] = ldg(src + e);
           }
         }
         r[it] = x;
@@ -241,20 +241,36 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLau
       sa.load(va, m0, (s + 1) * kBK);
       sb.load(vb, n0, (s + 1) * kBK);
     }
+    // Fragments are double-buffered in registers: the reads for k-group g+1
+    // are issued before the MFMAs of group g, so LDS latency hides behind them.
+    floatx4 fa[2][TM], fb[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[0][i] = SA::frag(bufA, wm + 32 * i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[0][j] = SB::frag(bufB, wn + 32 * j, 0, lane);
 #pragma unroll
     for (int g = 0; g < kBK / 8; ++g) {
-      floatx4 fa[TM], fb[TN];
+      const int c = g & 1;
+      if (g + 1 < kBK / 8) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = SA::frag(bufA, wm + 32 * i, g, lane);
+        for (int i = 0; i < TM; ++i) fa[c ^ 1][i] = SA::frag(bufA, wm + 32 * i, g + 1, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = SB::frag(bufB, wn + 32 * j, g, lane);
+        for (int j = 0; j < TN; ++j) fb[c ^ 1][j] = SB::frag(bufB, wn + 32 * j, g + 1, lane);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][q], fb[j][q], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
+    }
+    // Interleave: each LDS fragment read is placed between MFMAs, ahead of its use.
+#pragma unroll
+    for (int k = 0; k < (kBK / 2) * TM * TN / 4; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // up to two LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // three MFMAs
     }
     if (s + 1 < nstages) {
       float* nxt = lds + (cur ^ 1) * kStage;
@@ -332,11 +348,11 @@ struct EpiStore {
     }
     __device__ __forceinline__ float value(int row, int col, float v) const {
       float o = mult * v;
-      if (cin) o += beta * cin[(int64_t)row * B + col];
+      if (cin) o += beta * ldg(cin + (int64_t)row * B + col);
       if (ident) o = (row == col) ? 1.f : 0.f;
       return o;
     }
-    __device__ __forceinline__ void write(int row, int col, float o) { out[(int64_t)row * B + col] = o; }
+    __device__ __forceinline__ void write(int row, int col, float o) { stg(out + (int64_t)row * B + col, o); }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));
       return 0.f;
@@ -370,7 +386,7 @@ struct EpiStoreDesc {
       cols = ok ? d.cols : 0;
     }
     __device__ __forceinline__ float store(int row, int col, float v) {
-      if (row < rows && col < cols) p[(int64_t)row * ld + col] = v;
+      if (row < rows && col < cols) stg(p + (int64_t)row * ld + col, v);
       return 0.f;
     }
     __device__ void partial(int, float) {}
@@ -396,11 +412,11 @@ struct EpiNdbE {
     }
     __device__ __forceinline__ float store(int row, int col, float v) {
       const float d = (row == col) ? 1.f : 0.f;
-      e[(int64_t)row * B + col] = 1.5f * d - 0.5f * v;
+      stg(e + (int64_t)row * B + col, 1.5f * d - 0.5f * v);
       const float r = d - v;
       return r * r;
     }
-    __device__ void partial(int t, float s) { part[t] = s; }
+    __device__ void partial(int t, float s) { stg(part + t, s); }
   };
 };
 
@@ -433,12 +449,12 @@ struct EpiCnM {
     __device__ __forceinline__ float store(int row, int col, float v) {
       const int64_t idx = (int64_t)row * B + col;
       const float d = (row == col) ? 1.f : 0.f;
-      m[idx] = v;
-      c[idx] = (p1 * d - v) * pinv;
+      stg(m + idx, v);
+      stg(c + idx, (p1 * d - v) * pinv);
       const float r = d - v;
       return r * r;
     }
-    __device__ void partial(int t, float s) { part[t] = s; }
+    __device__ void partial(int t, float s) { stg(part + t, s); }
   };
 };
 
@@ -490,14 +506,14 @@ struct EpiClenshaw {
     __device__ __forceinline__ float value(int row, int col, float v) const {
       const int64_t idx = (int64_t)row * B + col;
       const float d = (row == col) ? cj : 0.f;
-      float o = mult * (d + k1 * v - k2 * b1[idx] - b2[idx]);
+      float o = mult * (d + k1 * v - k2 * ldg(b1 + idx) - ldg(b2 + idx));
       if (ident) o = (row == col) ? 1.f : 0.f;
       return o;
     }
     __device__ __forceinline__ void write(int row, int col, float o) {
       const int64_t idx = (int64_t)row * B + col;
-      out[idx] = o;
-      if (obf) obf[idx] = f32_to_bf16_bits(o);
+      stg(out + idx, o);
+      if (obf) stg(obf + idx, f32_to_bf16_bits(o));
     }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));

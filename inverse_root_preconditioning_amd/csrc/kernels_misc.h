@@ -207,9 +207,9 @@ __global__ void __launch_bounds__(256, 2) pi_step_kernel(const PiArgs P) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = m0 + rb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      const float v = (j < P.r) ? vv.p[(int64_t)row * P.ldv + j] * sj : 0.f;
+      const float v = (j < P.r) ? ldg(vv.p + (int64_t)row * P.ldv + j) * sj : 0.f;
       const float w = acc[e] * sj + eps * v;
-      if (!P.last) P.wout[(f * P.B + row) * kPiCols + j] = w;
+      if (!P.last) stg(P.wout + (f * P.B + row) * kPiCols + j, w);
       nsum += w * w;
       rsum += v * w;
     }
@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(256) ew_kernel(const EwArgs P) {
   const float pinv = 1.f / P.p, p1 = P.p + 1.f;
   float part = 0.f;
   for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
-    const floatx4 xv = *reinterpret_cast<const floatx4*>(P.x + off + 4 * i);
+    const floatx4 xv = ldg(reinterpret_cast<const floatx4*>(P.x + off + 4 * i));
     floatx4 o0, o1, o2;
     const int row = (int)((4 * i) / P.B);
     const int col0 = (int)(4 * i - (int64_t)row * P.B);
@@ -350,10 +350,10 @@ __global__ void __launch_bounds__(256) ew_kernel(const EwArgs P) {
         o0[e] = ident ? d : mult * (P.c0 * d + P.c1 * (2.f * y - d));
       }
     }
-    if (P.out0) *reinterpret_cast<floatx4*>(P.out0 + off + 4 * i) = o0;
+    if (P.out0) stg(reinterpret_cast<floatx4*>(P.out0 + off + 4 * i), o0);
     if (MODE == EW_NDB_START || MODE == EW_CN_START || MODE == EW_CHEBY_START)
-      *reinterpret_cast<floatx4*>(P.out1 + off + 4 * i) = o1;
-    if (MODE == EW_CHEBY_START) *reinterpret_cast<floatx4*>(P.out2 + off + 4 * i) = o2;
+      stg(reinterpret_cast<floatx4*>(P.out1 + off + 4 * i), o1);
+    if (MODE == EW_CHEBY_START) stg(reinterpret_cast<floatx4*>(P.out2 + off + 4 * i), o2);
   }
   if (P.partials != nullptr) {
     const float t = block_sum<256>(part, red);
