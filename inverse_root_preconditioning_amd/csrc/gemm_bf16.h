@@ -144,7 +144,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<E
   if constexpr (Epi::kSym) {
     static_assert(sizeof(lds) >= sizeof(float) * BM * (BN + 1), "LDS too small for the transpose");
     if (P.sym) {
-      sym_epilogue<TM, TN>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, lane, tm == tn);
+      sym_epilogue<TM, TN, 1>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, lane, tm == tn);
       return;
     }
   }

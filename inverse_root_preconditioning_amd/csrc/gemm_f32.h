@@ -4,7 +4,7 @@
 // Newton-DB update Y E and E Z, for instance, run as two jobs of one launch).
 // Each workgroup of 256 threads (4 waves, 2 x 2) owns one (64 TM) x (64 TN)
 // output tile of one item; each wave owns (32 TM) x (32 TN) of it as TM x TN
-// blocks of V_MFMA_F32_32X32X2_F32.  Operand tiles of 32 k-values are staged
+// blocks of V_MFMA_F32_32X32X2_F32.  Operand tiles of kBK k-values are staged
 // through LDS (double-buffered, one barrier per stage) from either a dense
 // stack of B x B row-major matrices or a table of block descriptors (zero
 // outside the block).  The epilogue turns the fp32 accumulators into the
@@ -23,7 +23,10 @@ namespace shp {
 enum { KCONTIG = 0, MNCONTIG = 1 };
 
 constexpr int kGemmThreads = 256;
-constexpr int kBK = 32;
+// k-depth of one LDS stage.  16 keeps a 128 x 128 tile's double-buffered
+// stages at 37 KB, so four workgroups fit a CU (measured faster than 32 with
+// two workgroups per CU at B = 1024).
+constexpr int kBK = 16;
 
 // One operand of a job: a dense stack (desc == nullptr) or descriptors.
 struct Operand {
@@ -60,12 +63,13 @@ __device__ __forceinline__ OperandView operand_view(const Operand& op, int64_t i
   return v;
 }
 
-// Tile staging for one operand: MN x 32 values (MN rows of the product).
-template <int MN, int LAYOUT, bool DESC>
+// Tile staging for one operand: MN x BK values (MN rows of the product).
+template <int MN, int LAYOUT, bool DESC, int BK = kBK>
 struct Stager {
-  static constexpr int kLoads = MN / 32;  // float4 per thread per stage
-  static constexpr int kStride = (LAYOUT == KCONTIG) ? (kBK + 4) : (MN + 4);
-  static constexpr int kFloats = (LAYOUT == KCONTIG) ? MN * (kBK + 4) : kBK * (MN + 4);
+  static constexpr int kLoads = MN * BK / 4 / kGemmThreads;  // float4 per thread per stage
+  static constexpr int kStride = (LAYOUT == KCONTIG) ? (BK + 4) : (MN + 4);
+  static constexpr int kFloats = (LAYOUT == KCONTIG) ? MN * (BK + 4) : BK * (MN + 4);
+  static_assert(kLoads >= 1, "tile too small for one float4 per thread");
   floatx4 r[kLoads];
 
   __device__ __forceinline__ void load(const OperandView& v, int mn0, int k0) {
@@ -75,8 +79,8 @@ struct Stager {
       const int idx = tid + kGemmThreads * it;
       int srow, scol;
       if (LAYOUT == KCONTIG) {
-        srow = mn0 + (idx >> 3);
-        scol = k0 + (idx & 7) * 4;
+        srow = mn0 + idx / (BK / 4);
+        scol = k0 + (idx % (BK / 4)) * 4;
       } else {
         srow = k0 + idx / (MN / 4);
         scol = mn0 + (idx % (MN / 4)) * 4;
@@ -107,7 +111,7 @@ struct Stager {
       const int idx = tid + kGemmThreads * it;
       int off;
       if (LAYOUT == KCONTIG)
-        off = (idx >> 3) * kStride + (idx & 7) * 4;
+        off = (idx / (BK / 4)) * kStride + (idx % (BK / 4)) * 4;
       else
         off = (idx / (MN / 4)) * kStride + (idx % (MN / 4)) * 4;
       *reinterpret_cast<floatx4*>(lds + off) = r[it];
@@ -143,16 +147,17 @@ struct GemmLaunch {
 };
 
 // Epilogue of a symmetric product (only tiles with tm <= tn are computed).
-// Each lane forms its outputs o = tile.value(...) at their own positions;
-// an off-diagonal tile writes them there and, through an LDS transpose,
-// coalesced at the mirrored positions; a diagonal tile writes its upper
-// triangle and mirrors it into the lower one.  `lds` must hold
-// 64 TM x (64 TN + 1) floats and be free (the main loop has ended with a
-// barrier).  The accumulator layout is that of the 32 x 32 MFMA blocks.
-template <int TM, int TN, class Tile>
+// Each lane forms its outputs o = tile.value(...) at their own positions and
+// writes them there (on a diagonal tile only the upper triangle).  The
+// mirrored half is written coalesced through an LDS transpose in PH phases
+// of 64 TM / PH tile rows (PH = 2 lets the waves of row group h stage their
+// rows in phase h), so `lds` needs (64 TM / PH) x (64 TN + 1) floats; it must
+// be free when this is called (the main loop has ended with a barrier).  The
+// accumulator layout is that of the 32 x 32 MFMA blocks, waves 2 x 2.
+template <int TM, int TN, int PH, class Tile>
 __device__ __forceinline__ void sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN], float* lds, int m0, int n0,
                                              int wm, int wn, int lane, bool diag) {
-  constexpr int BM = 64 * TM, BN = 64 * TN, LD = BN + 1;
+  constexpr int BN = 64 * TN, LD = BN + 1, RH = 64 * TM / PH;  // tile rows per phase
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -162,26 +167,41 @@ __device__ __forceinline__ void sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN]
         const int rl = wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         const int cl = wn + 32 * j + (lane & 31);
         const float o = tile.value(m0 + rl, n0 + cl, acc[i][j][e]);
-        if (!diag) tile.write(m0 + rl, n0 + cl, o);
-        lds[rl * LD + cl] = o;
+        if (!diag || rl <= cl) tile.write(m0 + rl, n0 + cl, o);
+        acc[i][j][e] = o;
       }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < BM * BN; idx += kGemmThreads) {
-    const int a = idx / BM, b = idx - (idx / BM) * BM;
-    if (!diag) {
-      tile.write(n0 + a, m0 + b, lds[b * LD + a]);  // (n0 + a, m0 + b) mirrors (m0 + b, n0 + a)
-    } else {
-      tile.write(m0 + a, m0 + b, (a <= b) ? lds[a * LD + b] : lds[b * LD + a]);
+#pragma unroll
+  for (int h = 0; h < PH; ++h) {
+    if (PH == 1 || wm / RH == h) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int rl = wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int cl = wn + 32 * j + (lane & 31);
+            lds[(rl - h * RH) * LD + cl] = acc[i][j][e];
+          }
     }
+    __syncthreads();
+    // o[h RH + b][a] goes to (n0 + a, m0 + h RH + b); on a diagonal tile only below the diagonal.
+    for (int idx = threadIdx.x; idx < RH * BN; idx += kGemmThreads) {
+      const int a = idx / RH, b = idx - (idx / RH) * RH;
+      if (!diag || a > h * RH + b) tile.write(n0 + a, m0 + h * RH + b, lds[b * LD + a]);
+    }
+    if (h + 1 < PH) __syncthreads();
   }
 }
 
-template <int TM, int TN, int LA, int LB, bool DA, bool DB, class Epi>
-__global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLaunch<Epi> P) {
+template <int TM, int TN, int LA, int LB, bool DA, bool DB, class Epi, int BK = kBK, int MINW = 2>
+__global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const GemmLaunch<Epi> P) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
-  using SA = Stager<BM, LA, DA>;
-  using SB = Stager<BN, LB, DB>;
-  __shared__ __attribute__((aligned(16))) float lds[2 * (SA::kFloats + SB::kFloats)];
+  using SA = Stager<BM, LA, DA, BK>;
+  using SB = Stager<BN, LB, DB, BK>;
+  constexpr int kPipe = 2 * (SA::kFloats + SB::kFloats);
+  constexpr int kTrans = Epi::kSym ? (BM / 2) * (BN + 1) : 0;  // the symmetric epilogue's transpose
+  __shared__ __attribute__((aligned(16))) float lds[kPipe > kTrans ? kPipe : kTrans];
   __shared__ float red[kGemmThreads / kWave];
 
   const uint32_t lid = xcd_remap(blockIdx.x, P.total);
@@ -226,7 +246,7 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLau
   SB sb;
   constexpr int kStage = SA::kFloats + SB::kFloats;
 
-  const int nstages = P.B / kBK;
+  const int nstages = P.B / BK;
   sa.load(va, m0, 0);
   sb.load(vb, n0, 0);
   sa.store(lds);
@@ -238,8 +258,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLau
     const float* bufA = lds + cur * kStage;
     const float* bufB = bufA + SA::kFloats;
     if (s + 1 < nstages) {
-      sa.load(va, m0, (s + 1) * kBK);
-      sb.load(vb, n0, (s + 1) * kBK);
+      sa.load(va, m0, (s + 1) * BK);
+      sb.load(vb, n0, (s + 1) * BK);
     }
     // Fragments are double-buffered in registers: the reads for k-group g+1
     // are issued before the MFMAs of group g, so LDS latency hides behind them.
@@ -249,9 +269,9 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLau
 #pragma unroll
     for (int j = 0; j < TN; ++j) fb[0][j] = SB::frag(bufB, wn + 32 * j, 0, lane);
 #pragma unroll
-    for (int g = 0; g < kBK / 8; ++g) {
+    for (int g = 0; g < BK / 8; ++g) {
       const int c = g & 1;
-      if (g + 1 < kBK / 8) {
+      if (g + 1 < BK / 8) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) fa[c ^ 1][i] = SA::frag(bufA, wm + 32 * i, g + 1, lane);
 #pragma unroll
@@ -265,13 +285,6 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLau
           for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
     }
-    // Interleave: each LDS fragment read is placed between MFMAs, ahead of its use.
-#pragma unroll
-    for (int k = 0; k < (kBK / 2) * TM * TN / 4; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // up to two LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // three MFMAs
-    }
     if (s + 1 < nstages) {
       float* nxt = lds + (cur ^ 1) * kStage;
       sa.store(nxt);
@@ -284,9 +297,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2) gemm_f32_kernel(const GemmLau
   // row = 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = 32 j + lane % 32.
   typename Epi::Tile tile(P.e[job], item, P.B);
   if constexpr (Epi::kSym) {
-    static_assert(2 * (SA::kFloats + SB::kFloats) >= BM * (BN + 1), "LDS too small for the transpose");
     if (P.sym) {
-      sym_epilogue<TM, TN>(tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
+      sym_epilogue<TM, TN, kPipe >= BM * (BN + 1) ? 1 : 2>(tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
       return;
     }
   }

@@ -109,8 +109,9 @@ template <int PANEL>
 __global__ void __launch_bounds__(256, 2) pi_step_kernel(const PiArgs P) {
   constexpr int RB = PANEL / 32;  // row blocks per panel
   constexpr int KS = 4 / RB;      // waves sharing a row block (k split)
-  using SA = Stager<PANEL, KCONTIG, false>;
-  using SV = Stager<kPiCols, MNCONTIG, true>;
+  constexpr int BK = 32;
+  using SA = Stager<PANEL, KCONTIG, false, BK>;
+  using SV = Stager<kPiCols, MNCONTIG, true, BK>;
   __shared__ __attribute__((aligned(16))) float lds[2 * (SA::kFloats + SV::kFloats)];
   __shared__ float s_col[kPiCols];
   __shared__ float colsum[2][RB][kPiCols];
@@ -157,7 +158,7 @@ __global__ void __launch_bounds__(256, 2) pi_step_kernel(const PiArgs P) {
   SA sa;
   SV sv;
   const int stage = SA::kFloats + SV::kFloats;
-  const int nstages = P.B / kBK;
+  const int nstages = P.B / BK;
   sa.load(va, m0, 0);
   sv.load(vv, 0, 0);
   sa.store(lds);
@@ -168,11 +169,11 @@ __global__ void __launch_bounds__(256, 2) pi_step_kernel(const PiArgs P) {
     float* bufA = lds + cur * stage;
     float* bufV = bufA + SA::kFloats;
     if (s + 1 < nstages) {
-      sa.load(va, m0, (s + 1) * kBK);
-      sv.load(vv, 0, (s + 1) * kBK);
+      sa.load(va, m0, (s + 1) * BK);
+      sv.load(vv, 0, (s + 1) * BK);
     }
 #pragma unroll
-    for (int gg = 0; gg < kBK / 8 / KS; ++gg) {
+    for (int gg = 0; gg < BK / 8 / KS; ++gg) {
       const int g = gg * KS + ks;
       const floatx4 fa = SA::frag(bufA, rb * 32, g, lane);
       const floatx4 fv = SV::frag(bufV, 0, g, lane);
