@@ -359,6 +359,40 @@ def precondition(XL, G, XR):
     return _f64(XL) @ _f64(G) @ _f64(XR)
 
 
+def adam_direction(m, v, g, beta1, beta2, eps, step):
+    """Adam's moments and direction for one block (step >= 1).
+
+    [DASH] "Step-by-step", grafting: the length of the update is borrowed
+    from an Adam-like direction P.  Reading: plain Adam with bias
+    correction,
+        m <- beta1 m + (1 - beta1) g,   v <- beta2 v + (1 - beta2) g^2,
+        P = (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps).
+    Returns (m, v, P).
+    """
+    g = _f64(g)
+    m = beta1 * _f64(m) + (1.0 - beta1) * g
+    v = beta2 * _f64(v) + (1.0 - beta2) * g * g
+    mhat = m / (1.0 - beta1 ** step)
+    vhat = v / (1.0 - beta2 ** step)
+    return m, v, mhat / (np.sqrt(vhat) + eps)
+
+
+def graft_update(theta, m, v, g, U, lr, beta1, beta2, eps, step):
+    """Grafted parameter update of one block.
+
+    [DASH] "Step-by-step", grafting: with U the preconditioned gradient and
+    P the Adam-like direction, s = ||P||_F / ||U||_F and theta <- theta -
+    lr * s * U.  Readings: the norms are taken per block (U is formed per
+    block); s = 0 when ||U||_F = 0 (then U = 0 and the step is zero anyway).
+    Returns (theta, m, v, s).
+    """
+    m, v, P = adam_direction(m, v, g, beta1, beta2, eps, step)
+    U = _f64(U)
+    nu = math.sqrt(float(np.sum(U * U)))
+    s = math.sqrt(float(np.sum(P * P))) / nu if nu > 0.0 else 0.0
+    return _f64(theta) - lr * s * U, m, v, s
+
+
 def relative_frobenius(x, ref):
     """||x - ref||_F / ||ref||_F, the parity measure."""
     x = _f64(x)

@@ -361,3 +361,45 @@ def test_ndb_single_pass_is_inverse_square_root():
     sc = O.scale_factor(A, 0.0, "power", V0, 30)
     X = O.invroot(A, sc, "ndb", iters=30, p=2)
     assert O.relative_frobenius(X, O.invroot_exact(A, 2)) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Grafting
+# ---------------------------------------------------------------------------
+
+def test_adam_direction_first_step_closed_form():
+    g = np.array([[0.5, -2.0], [0.0, 1e-3]])
+    _, _, P = O.adam_direction(np.zeros((2, 2)), np.zeros((2, 2)), g, 0.9, 0.999, 1e-8, 1)
+    # after one step m_hat = g and v_hat = g^2 exactly, so P = g / (|g| + eps)
+    assert np.allclose(P, g / (np.abs(g) + 1e-8), rtol=1e-15, atol=0)
+
+
+def test_graft_matches_torch_adam_when_u_is_parallel_to_p():
+    """If U = c P (c > 0) then s U = P and the grafted step is exactly Adam's;
+    torch.optim.Adam (CPU, float64) is the reference."""
+    import torch
+    gen = np.random.default_rng(19)
+    theta = gen.standard_normal((6, 5))
+    m = np.zeros((6, 5))
+    v = np.zeros((6, 5))
+    tp = torch.nn.Parameter(torch.tensor(theta, dtype=torch.float64))
+    opt = torch.optim.Adam([tp], lr=3e-3, betas=(0.9, 0.95), eps=1e-8)
+    for step in (1, 2, 3):
+        g = gen.standard_normal((6, 5))
+        _, _, P = O.adam_direction(m, v, g, 0.9, 0.95, 1e-8, step)
+        theta, m, v, s = O.graft_update(theta, m, v, g, 2.5 * P, 3e-3, 0.9, 0.95, 1e-8, step)
+        assert abs(s - 0.4) <= 1e-14
+        tp.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        assert np.allclose(theta, tp.detach().numpy(), rtol=0, atol=1e-14)
+
+
+def test_graft_step_length_and_zero_update():
+    gen = np.random.default_rng(20)
+    theta, g, U = gen.standard_normal((3, 8, 8))
+    new, _, _, s = O.graft_update(theta, np.zeros((8, 8)), np.zeros((8, 8)), g, U, 0.1, 0.9, 0.999, 1e-8, 1)
+    _, _, P = O.adam_direction(np.zeros((8, 8)), np.zeros((8, 8)), g, 0.9, 0.999, 1e-8, 1)
+    assert abs(np.linalg.norm(new - theta) - 0.1 * np.linalg.norm(P)) <= 1e-12
+    same, _, _, s0 = O.graft_update(theta, np.zeros((8, 8)), np.zeros((8, 8)), g, np.zeros((8, 8)),
+                                    0.1, 0.9, 0.999, 1e-8, 1)
+    assert s0 == 0.0 and np.array_equal(same, theta)
