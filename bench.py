@@ -197,6 +197,19 @@ def main(argv=None):
     torch.cuda.synchronize()
     stages = {k: ev[i].elapsed_time(ev[i + 1]) for i, k in
               enumerate(["accumulate", "scale", "invroot", "precondition"])}
+    # Grafted parameter update (reported beside the step, not part of it).
+    params = [t.clone() for t in tens]
+    moms = [torch.zeros_like(t) for t in tens]
+    vels = [torch.zeros_like(t) for t in tens]
+    gtabs = [table, utable] + [PL.BlockTable(_entries(ts, B)[:n], B) for ts in (params, moms, vels)]
+    PL.graft_update(*gtabs, 1e-3, 0.9, 0.95, 1e-8, 1)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record()
+    PL.graft_update(*gtabs, 1e-3, 0.9, 0.95, 1e-8, 2)
+    g1.record()
+    torch.cuda.synchronize()
+    graft_ms = g0.elapsed_time(g1)
+    del params, moms, vels, gtabs
 
     # Timing hook on the dominant kernel during the timed steps.
     # Algorithmic flops of one product: 2 B^3 in full; a symmetric product
@@ -270,6 +283,7 @@ def main(argv=None):
                      "flops_per_launch": flops_per_launch,
                      "mfma_tflops_executed": round(mfma_flops / (avg_ms * 1e-3) / 1e12, 2)},
         "stages_ms": {k: round(v, 3) for k, v in stages.items()},
+        "graft_update_ms": round(graft_ms, 3),
         "invroot_blocks_per_s": round(nf / (stages["invroot"] * 1e-3), 2),
         "status_nonzero_factors": int((status != 0).sum()),
     }

@@ -9,6 +9,7 @@
  *   shampoo_invroot_newton   X ~ c^{-1/p} ((F + eps I)/c)^{-1/p} by Newton-DB or coupled Newton
  *   shampoo_invroot_cheby    the same by a Chebyshev polynomial evaluated with Clenshaw
  *   shampoo_precondition     U = X_L G X_R
+ *   shampoo_graft_update     theta <- theta - lr (||P||/||U||) U with P Adam's direction
  *
  * Sources (cited by page title and section): "DASH: Faster Shampoo via Batched
  * Block Preconditioning and Efficient Inverse-Root Solvers", the howistudyai.com
@@ -99,7 +100,8 @@ enum {
   SHAMPOO_OP_SCALE = 2,
   SHAMPOO_OP_NEWTON = 3,
   SHAMPOO_OP_CHEBY = 4,
-  SHAMPOO_OP_PRECONDITION = 5
+  SHAMPOO_OP_PRECONDITION = 5,
+  SHAMPOO_OP_GRAFT = 6
 };
 
 /* A B x B block inside a larger row-major fp32 matrix (a layer gradient or
@@ -228,9 +230,33 @@ int shampoo_precondition(const float* x_roots, const shampoo_block* g_blocks,
                          int64_t nblocks, int B, const shampoo_block* u_blocks, int prec,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * shampoo_graft_update -- grafted parameter update of every block.
+ * [DASH] "Step-by-step", grafting: the update keeps the Shampoo direction U
+ * and takes its length from an Adam-like direction P.
+ *
+ *   Per block (elementwise over the block's rows x cols, taken from g_blocks):
+ *     m <- beta1 m + (1 - beta1) g;  v <- beta2 v + (1 - beta2) g^2          (in place)
+ *     P = (m / (1 - beta1^step)) / (sqrt(v / (1 - beta2^step)) + eps)
+ *     s = ||P||_F / ||U||_F  (0 when ||U||_F = 0)
+ *     theta <- theta - lr s U                                              (in place)
+ *   g_blocks, u_blocks (U from shampoo_precondition), param_blocks, m_blocks,
+ *   v_blocks   device arrays [nblocks] of descriptors of blocks of the same shape;
+ *              the m and v blocks hold Adam's state (zeros before step 1)
+ *   step       1-based step count for the bias corrections;  0 <= beta1, beta2 < 1;  eps >= 0
+ *   scale_out  NULL or device float[nblocks]: s of every block
+ *   ws         shampoo_workspace_bytes(SHAMPOO_OP_GRAFT, nblocks, B, 0, SHAMPOO_F32)
+ */
+int shampoo_graft_update(const shampoo_block* g_blocks, const shampoo_block* u_blocks,
+                         const shampoo_block* param_blocks, const shampoo_block* m_blocks,
+                         const shampoo_block* v_blocks, int64_t nblocks, int B, float lr, float beta1,
+                         float beta2, float eps, int step, float* scale_out,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Workspace size in bytes for an operation (op = SHAMPOO_OP_*).  `count` is
  * nfactors for SCALE/NEWTON/CHEBY and nblocks for ACCUMULATE/PRECONDITION;
- * `variant_or_degree` is the Newton variant or the Chebyshev degree (else 0).
+ * `variant_or_degree` is the Newton variant or the Chebyshev degree (else 0);
+ * `count` is nblocks for GRAFT too.
  * Returns 0 for invalid arguments as well as for operations that need none. */
 size_t shampoo_workspace_bytes(int op, int64_t count, int B, int variant_or_degree, int prec);
 

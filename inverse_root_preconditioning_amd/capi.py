@@ -43,6 +43,7 @@ OP_SCALE = 2
 OP_NEWTON = 3
 OP_CHEBY = 4
 OP_PRECONDITION = 5
+OP_GRAFT = 6
 
 ABI_VERSION = 1
 
@@ -82,6 +83,9 @@ _SIGNATURES = {
     "shampoo_invroot_cheby": (c_int, [c_void_p, c_void_p, c_int64, c_int, c_int, c_int, c_double, c_int,
                                       c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "shampoo_precondition": (c_int, [c_void_p, c_void_p, c_int64, c_int, c_void_p, c_int,
+                                     c_void_p, c_size_t, c_void_p]),
+    "shampoo_graft_update": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int,
+                                     c_float, c_float, c_float, c_float, c_int, c_void_p,
                                      c_void_p, c_size_t, c_void_p]),
 }
 
@@ -165,3 +169,9 @@ def shampoo_timing_hook(family, events, capacity):
 
 def shampoo_timing_count():
     return load().shampoo_timing_count()
+
+
+def shampoo_graft_update(g_blocks, u_blocks, param_blocks, m_blocks, v_blocks, nblocks, B, lr, beta1, beta2,
+                         eps, step, scale_out, ws, ws_bytes, stream):
+    return load().shampoo_graft_update(g_blocks, u_blocks, param_blocks, m_blocks, v_blocks, nblocks, B, lr,
+                                       beta1, beta2, eps, step, scale_out, ws, ws_bytes, stream)

@@ -378,3 +378,97 @@ __global__ void __launch_bounds__(64) resid_kernel(const float* __restrict__ par
 }
 
 }  // namespace shp
+
+namespace shp {
+
+// ---------------------------------------------------------------------------
+// Grafting with Adam's magnitude, per block: m, v <- Adam moments of g;
+// P = (m bc1) / (sqrt(v bc2) + eps); s = ||P||_F / ||U||_F (0 if U = 0);
+// theta <- theta - lr s U.  Pass 1 updates m, v and writes per-chunk partial
+// sums of P^2 and U^2; pass 2 forms s in a fixed order and applies it.  A
+// chunk is a range of block rows; all five descriptor tables describe blocks
+// of the same shape (the gradient's rows x cols).
+// ---------------------------------------------------------------------------
+struct GraftArgs {
+  const shampoo_block* g;
+  const shampoo_block* u;
+  const shampoo_block* theta;
+  const shampoo_block* m;
+  const shampoo_block* v;
+  float beta1, beta2, eps, bc1, bc2, lr;
+  float* partials;   // [nblocks][chunks][2]
+  float* scale_out;  // [nblocks] or null
+  int B;
+  int chunks;
+};
+
+__device__ __forceinline__ bool graft_block_ok(const shampoo_block& d, int B) {
+  return d.ptr != nullptr && d.rows >= 0 && d.cols >= 0 && d.rows <= B && d.cols <= B && d.ld >= d.cols;
+}
+
+__global__ void __launch_bounds__(256) graft_moments_kernel(const GraftArgs P) {
+  __shared__ float red[4];
+  const int64_t blk = blockIdx.x / P.chunks;
+  const int chunk = blockIdx.x - (int)(blk * P.chunks);
+  const shampoo_block g = P.g[blk], u = P.u[blk], m = P.m[blk], v = P.v[blk];
+  const bool ok = graft_block_ok(g, P.B) && graft_block_ok(u, P.B) && graft_block_ok(m, P.B) &&
+                  graft_block_ok(v, P.B) && u.rows >= g.rows && u.cols >= g.cols && m.rows >= g.rows &&
+                  m.cols >= g.cols && v.rows >= g.rows && v.cols >= g.cols;
+  const int rows = ok ? g.rows : 0, cols = ok ? g.cols : 0;
+  const int per = (P.B + P.chunks - 1) / P.chunks;
+  const int r0 = chunk * per, r1 = min(rows, r0 + per);
+  float sp = 0.f, su = 0.f;
+  for (int r = r0; r < r1; ++r) {
+    for (int c = threadIdx.x; c < cols; c += 256) {
+      const float gg = ldg(g.ptr + (int64_t)r * g.ld + c);
+      float* mp = m.ptr + (int64_t)r * m.ld + c;
+      float* vp = v.ptr + (int64_t)r * v.ld + c;
+      const float mm = P.beta1 * ldg(mp) + (1.f - P.beta1) * gg;
+      const float vv = P.beta2 * ldg(vp) + (1.f - P.beta2) * gg * gg;
+      stg(mp, mm);
+      stg(vp, vv);
+      const float p = (mm * P.bc1) / (sqrtf(vv * P.bc2) + P.eps);
+      const float uu = ldg(u.ptr + (int64_t)r * u.ld + c);
+      sp += p * p;
+      su += uu * uu;
+    }
+  }
+  const float tp = block_sum<256>(sp, red);
+  const float tu = block_sum<256>(su, red);
+  if (threadIdx.x == 0) {
+    stg(P.partials + (blk * P.chunks + chunk) * 2, tp);
+    stg(P.partials + (blk * P.chunks + chunk) * 2 + 1, tu);
+  }
+}
+
+__global__ void __launch_bounds__(256) graft_apply_kernel(const GraftArgs P) {
+  __shared__ float s_sh;
+  const int64_t blk = blockIdx.x / P.chunks;
+  const int chunk = blockIdx.x - (int)(blk * P.chunks);
+  if (threadIdx.x == 0) {
+    float np2 = 0.f, nu2 = 0.f;
+    for (int c = 0; c < P.chunks; ++c) {
+      np2 += P.partials[(blk * P.chunks + c) * 2];
+      nu2 += P.partials[(blk * P.chunks + c) * 2 + 1];
+    }
+    const float s = (nu2 > 0.f) ? sqrtf(np2) / sqrtf(nu2) : 0.f;
+    s_sh = s;
+    if (chunk == 0 && P.scale_out != nullptr) stg(P.scale_out + blk, s);
+  }
+  __syncthreads();
+  const float step = P.lr * s_sh;
+  const shampoo_block g = P.g[blk], u = P.u[blk], th = P.theta[blk];
+  const bool ok = graft_block_ok(g, P.B) && graft_block_ok(u, P.B) && graft_block_ok(th, P.B) &&
+                  u.rows >= g.rows && u.cols >= g.cols && th.rows >= g.rows && th.cols >= g.cols;
+  const int rows = ok ? g.rows : 0, cols = ok ? g.cols : 0;
+  const int per = (P.B + P.chunks - 1) / P.chunks;
+  const int r0 = chunk * per, r1 = min(rows, r0 + per);
+  for (int r = r0; r < r1; ++r) {
+    for (int c = threadIdx.x; c < cols; c += 256) {
+      float* tp = th.ptr + (int64_t)r * th.ld + c;
+      stg(tp, ldg(tp) - step * ldg(u.ptr + (int64_t)r * u.ld + c));
+    }
+  }
+}
+
+}  // namespace shp

@@ -251,6 +251,19 @@ size_t precond_layout(Carver& c, int64_t n, int B, int prec, PrecondWs* out) {
   return c.off;
 }
 
+int graft_chunks(int B) {
+  int c = B / 64;
+  if (c < 1) c = 1;
+  if (c > 64) c = 64;
+  return c;
+}
+
+size_t graft_layout(Carver& c, int64_t n, int B, float** partials) {
+  float* p = c.take<float>((size_t)n * graft_chunks(B) * 2);
+  if (partials) *partials = p;
+  return c.off;
+}
+
 struct AccumWs {
   uint16_t* g16;   // bf16 G
   uint16_t* gt16;  // bf16 G^T
@@ -720,6 +733,7 @@ size_t shampoo_workspace_bytes(int op, int64_t count, int B, int variant_or_degr
       return newton_layout(c, count, B, variant_or_degree, nullptr);
     case SHAMPOO_OP_CHEBY: return cheby_layout(c, count, B, prec, nullptr);
     case SHAMPOO_OP_PRECONDITION: return precond_layout(c, count, B, prec, nullptr);
+    case SHAMPOO_OP_GRAFT: return graft_layout(c, count, B, nullptr);
     default: return 0;
   }
 }
@@ -913,3 +927,45 @@ int shampoo_precondition(const float* x_roots, const shampoo_block* g_blocks, in
 }
 
 }  // extern "C"
+
+extern "C" int shampoo_graft_update(const shampoo_block* g_blocks, const shampoo_block* u_blocks,
+                                    const shampoo_block* param_blocks, const shampoo_block* m_blocks,
+                                    const shampoo_block* v_blocks, int64_t nblocks, int B, float lr, float beta1,
+                                    float beta2, float eps, int step, float* scale_out, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  if (nblocks < 0) return SHAMPOO_EINVAL;
+  if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
+  if (!std::isfinite(lr) || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps >= 0.f) ||
+      !std::isfinite(eps) || step < 1)
+    return SHAMPOO_EINVAL;
+  if (nblocks == 0) return SHAMPOO_OK;
+  if (!g_blocks || !u_blocks || !param_blocks || !m_blocks || !v_blocks) return SHAMPOO_EINVAL;
+  Carver cm(nullptr);
+  const size_t need = graft_layout(cm, nblocks, B, nullptr);
+  if (ws == nullptr || ws_bytes < need) return SHAMPOO_EWORKSPACE;
+  const int chunks = graft_chunks(B);
+  if ((uint64_t)nblocks * chunks > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
+  Carver c(ws);
+  GraftArgs a;
+  memset(&a, 0, sizeof(a));
+  graft_layout(c, nblocks, B, &a.partials);
+  a.g = g_blocks;
+  a.u = u_blocks;
+  a.theta = param_blocks;
+  a.m = m_blocks;
+  a.v = v_blocks;
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.eps = eps;
+  a.bc1 = (float)(1.0 / (1.0 - std::pow((double)beta1, (double)step)));
+  a.bc2 = (float)(1.0 / (1.0 - std::pow((double)beta2, (double)step)));
+  a.lr = lr;
+  a.scale_out = scale_out;
+  a.B = B;
+  a.chunks = chunks;
+  const dim3 grid((uint32_t)(nblocks * chunks));
+  hipLaunchKernelGGL(graft_moments_kernel, grid, dim3(256), 0, stream, a);
+  SHP_TRY(check_launch());
+  hipLaunchKernelGGL(graft_apply_kernel, grid, dim3(256), 0, stream, a);
+  return check_launch();
+}

@@ -160,6 +160,20 @@ def precondition(x_roots, g_table, u_table, prec=F32, ws=None, stream=None):
                                          _stream(stream)), "shampoo_precondition")
 
 
+def graft_update(g_table, u_table, p_table, m_table, v_table, lr, beta1, beta2, eps, step, scale_out=None,
+                 ws=None, stream=None):
+    """theta <- theta - lr (||P||_F / ||U||_F) U per block, P Adam's direction (m, v updated)."""
+    n, B = g_table.n, g_table.B
+    for t in (u_table, p_table, m_table, v_table):
+        if t.n != n or t.B != B:
+            raise ValueError("descriptor tables differ in size")
+    ws = ws or Workspace(g_table.tensor.device)
+    wp, wb = ws.get(capi.shampoo_workspace_bytes(capi.OP_GRAFT, n, B, 0, F32))
+    capi.check(capi.shampoo_graft_update(g_table.ptr, u_table.ptr, p_table.ptr, m_table.ptr, v_table.ptr, n, B,
+                                         lr, beta1, beta2, eps, step, _ptr(scale_out), wp, wb, _stream(stream)),
+               "shampoo_graft_update")
+
+
 @dataclass
 class StepConfig:
     """One optimizer step of the block preconditioner (defaults: the pages'

@@ -116,6 +116,19 @@ def test_validation_codes_without_gpu():
     assert f.shampoo_precondition(FAKE, 0, 2, 64, FAKE, f.F32, FAKE, 1 << 40, 0) == f.EINVAL
 
 
+def test_graft_validation_without_gpu():
+    f = capi
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 3, 128)
+    assert f.shampoo_graft_update(*ok, 1e-3, 0.9, 0.999, 1e-8, 0, 0, FAKE, 1 << 40, 0) == f.EINVAL   # step 0
+    assert f.shampoo_graft_update(*ok, 1e-3, 1.0, 0.999, 1e-8, 1, 0, FAKE, 1 << 40, 0) == f.EINVAL   # beta1 = 1
+    assert f.shampoo_graft_update(*ok, float("inf"), 0.9, 0.999, 1e-8, 1, 0, FAKE, 1 << 40, 0) == f.EINVAL
+    assert f.shampoo_graft_update(*ok, 1e-3, 0.9, 0.999, 1e-8, 1, 0, FAKE, 0, 0) == f.EWORKSPACE
+    assert f.shampoo_graft_update(0, FAKE, FAKE, FAKE, FAKE, 3, 128, 1e-3, 0.9, 0.999, 1e-8, 1, 0, FAKE,
+                                  1 << 40, 0) == f.EINVAL
+    assert f.shampoo_graft_update(0, 0, 0, 0, 0, 0, 128, 1e-3, 0.9, 0.999, 1e-8, 1, 0, 0, 0, 0) == f.OK
+    assert f.shampoo_workspace_bytes(f.OP_GRAFT, 10, 1024, 0, f.F32) >= 10 * 16 * 2 * 4
+
+
 def test_binding_raises_when_library_missing(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         capi.load(str(tmp_path / "missing.so"))
