@@ -30,7 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_F32_MFMA = 157.3     # TFLOP/s, MI355X dense fp32 matrix
-PEAK_BF16_MFMA = 2500.0   # TFLOP/s, MI355X dense bf16 matrix
+PEAK_BF16_MFMA = 2500.0   # TFLOP/s, MI355X dense bf16 (and fp16) matrix
 METRIC = "inverse-4th-root blocks/s at B=1024 fp32 + optimizer-step ms; % MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["common.h", "gemm_f32.h", "gemm_bf16.h", "kernels_misc.h", "shampoo.hip"]
@@ -61,6 +61,13 @@ def workloads():
                          prec=capi.F32, nblocks=36,
                          name="one GPU's share of 8 of the 360M-shaped step: 36 blocks (72 factors) of "
                               "1024^2, Newton-DB k=10, fp32"),
+        "c3-cn": dict(cfg=3, spec=W.MODEL_360M, B=1024, solver="newton", variant=capi.CN, iters=10,
+                      prec=capi.F32, nblocks=None,
+                      name="360M-shaped optimizer step, B=1024, 576 factors, coupled Newton k=10, fp32"),
+        "c3-cn16": dict(cfg=3, spec=W.MODEL_360M, B=1024, solver="newton", variant=capi.CN_F16, iters=10,
+                        prec=capi.F32, nblocks=None,
+                        name="360M-shaped optimizer step, B=1024, 576 factors, coupled Newton k=10 on fp16 "
+                             "operands with fp32 accumulation (accumulate, scale, precondition fp32)"),
         "c5": dict(cfg=5, spec=W.MODEL_1_3B, B=2048, solver="cheby", variant=capi.NDB, degree=24, iters=0,
                    prec=capi.BF16_IN, nblocks=None,
                    name="1.3B-shaped optimizer step: 24 layers, hidden 2048, MLP 8192; B=2048, 288 blocks "
@@ -134,7 +141,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="c3", choices=["c3", "c3-literal", "c3-share", "c5"])
+    ap.add_argument("--workload", default="c3", choices=["c3", "c3-literal", "c3-share", "c3-cn", "c3-cn16", "c5"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -218,7 +225,15 @@ def main(argv=None):
     sym_product = float(B) * B * (B + 1)
     tiles = B // 128 if B % 128 == 0 else B // 64
     executed = 2.0 * B ** 3 * (tiles * (tiles + 1) / 2) / tiles ** 2  # upper tiles incl. the diagonal ones
-    if cfg.solver == "newton":
+    if cfg.solver == "newton" and cfg.variant in (capi.CN, capi.CN_F16):
+        family, per_step = capi.TIME_CN_M, cfg.iters - 1
+        flops_per_launch = nf * 2.0 * B ** 3
+        mfma_flops = flops_per_launch
+        half = cfg.variant == capi.CN_F16
+        peak = PEAK_BF16_MFMA if half else PEAK_F32_MFMA
+        kname = ("gemm_h16_nt_kernel<EpiCnM, fp16>" if half else "gemm_f32_kernel<EpiCnM>") + \
+            " (coupled Newton C^p M, one full product per factor)"
+    elif cfg.solver == "newton":
         family, per_step = capi.TIME_NDB_PAIR, 2 * (cfg.iters - 2)
         flops_per_launch = 2 * nf * sym_product
         mfma_flops = 2 * nf * executed
@@ -274,7 +289,8 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16-in/f32" if cfg.prec == capi.BF16_IN else "f32",
+        "dtype": ("bf16-in/f32" if cfg.prec == capi.BF16_IN else
+                  "f16-in/f32" if cfg.variant == capi.CN_F16 and cfg.solver == "newton" else "f32"),
         "data": "synthetic N(0, 0.02^2) gradients of the workload's weight shapes, seeded",
         "config": {"workload": wl["name"], "B": B, "blocks": n, "factors": nf},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",

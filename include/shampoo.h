@@ -82,7 +82,8 @@ enum {
 enum {
   SHAMPOO_NDB = 0,            /* Newton-DB, second pass on Y (the pages' chaining) */
   SHAMPOO_NDB_Z = 1,          /* Newton-DB, second pass on Z_1 / (3/2)^iters (a variant) */
-  SHAMPOO_CN = 2              /* coupled Newton */
+  SHAMPOO_CN = 2,             /* coupled Newton */
+  SHAMPOO_CN_F16 = 3          /* coupled Newton on fp16 operands, fp32 accumulate (B % 128 == 0) */
 };
 
 /* Modifier bit, OR-ed into `variant` (shampoo_invroot_newton) or `prec`
@@ -180,6 +181,10 @@ int shampoo_scale_power(const float* factors, int64_t nfactors, int B, float eps
  *           SHAMPOO_NDB_Z: p = 4: s = (3/2)^iters, X = sqrt(s) pass(pass(A_s).Z / s).Y
  *           SHAMPOO_CN:    X = I, M = A_s; iters times { C = ((p+1) I - M)/p;
  *                          X <- X C; M <- C^p M };  p in {1, 2, 4, 8}
+ *           SHAMPOO_CN_F16: the same iteration with every product on fp16
+ *                          operands (RNE) and fp32 accumulation; only fp16
+ *                          copies of the iterates are kept, X is written in fp32
+ *                          ([DASH] Scoreboard: coupled Newton in FP16)
  *   iters      iterations per pass, 1..100
  *   x_out      device float[nfactors][B][B]
  *   resid_out  NULL or device float[nfactors][passes * iters]: ||I - Z Y||_F before
@@ -271,7 +276,8 @@ enum {
   SHAMPOO_TIME_OFF = 0,
   SHAMPOO_TIME_NDB_PAIR = 1,   /* Newton-DB updates Y E and E Z, launched together (2 products) */
   SHAMPOO_TIME_NDB_P = 2,      /* Newton-DB product Z Y with the E = (3I - P)/2 epilogue */
-  SHAMPOO_TIME_CLENSHAW = 3    /* one Clenshaw product A_s b (fp32 or bf16) */
+  SHAMPOO_TIME_CLENSHAW = 3,   /* one Clenshaw product A_s b (fp32 or bf16) */
+  SHAMPOO_TIME_CN_M = 4        /* coupled Newton's product C^p M (fp32 or fp16) */
 };
 
 /*

@@ -35,6 +35,7 @@ SCALE_FROBENIUS = 1
 NDB = 0
 NDB_Z = 1
 CN = 2
+CN_F16 = 3
 # Modifier bit for variant (newton) / prec (cheby): compute symmetric products in full
 FULL_PRODUCTS = 0x100
 # Workspace op ids
@@ -67,6 +68,7 @@ TIME_OFF = 0
 TIME_NDB_PAIR = 1
 TIME_NDB_P = 2
 TIME_CLENSHAW = 3
+TIME_CN_M = 4
 
 _SIGNATURES = {
     "shampoo_abi_version": (c_int, []),

@@ -75,6 +75,18 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
   return (uint16_t)(u >> 16);
 }
 
+// fp32 -> fp16 bits, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// 16-bit operand formats of the half-width MFMA products.
+enum { H16_BF16 = 0, H16_F16 = 1 };
+
+__device__ __forceinline__ uint16_t to_h16(float x, int fmt) {
+  return fmt == H16_F16 ? f32_to_f16_bits(x) : f32_to_bf16_bits(x);
+}
+
 __device__ __forceinline__ bool degenerate(int32_t st) {
   return (st & (SHAMPOO_BLK_ZERO | SHAMPOO_BLK_NONPOS_RQ)) != 0;
 }

@@ -1,8 +1,9 @@
-// bf16-input batched products for gfx950 (V_MFMA_F32_32X32X16_BF16, fp32
-// accumulate) and the casts that prepare their operands.
+// Half-width-input batched products for gfx950 (V_MFMA_F32_32X32X16_BF16 and
+// V_MFMA_F32_32X32X16_F16, fp32 accumulate) and the casts that prepare their
+// operands.
 //
-// Every bf16 product here is in "NT" form, C_i = A_i Bt_i^T with A and Bt
-// row-major bf16 stacks, so both operands are read along k with 16-byte
+// Every 16-bit product here is in "NT" form, C_i = A_i Bt_i^T with A and Bt
+// row-major 16-bit stacks, so both operands are read along k with 16-byte
 // loads.  Operands that are needed transposed are produced transposed by
 // the cast kernels (or by the epilogue of the previous step).  Tiles are
 // 128 x 128 per workgroup (4 waves of 64 x 64), k staged 64 at a time.
@@ -34,33 +35,48 @@ struct EpiStoreBf16 {
 };
 
 template <class Epi>
-struct Bf16Launch {
-  const uint16_t* a;
-  const uint16_t* bt;
-  typename Epi::Job e;
-  int64_t nitems;
+struct H16Launch {
+  const uint16_t* a[2];
+  const uint16_t* bt[2];
+  typename Epi::Job e[2];
+  int64_t nitems;      // items per job
   int B;
   int tiles_n;
   int tiles_per_item;
   int sym;
-  uint32_t total;
+  uint32_t total;      // njobs * nitems * tiles_per_item
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &u, sizeof(r));
-  return r;
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+template <int FMT>
+__device__ __forceinline__ floatx16 mfma_h16(const u32x4& a, const u32x4& b, const floatx16& c) {
+  if constexpr (FMT == H16_F16) {
+    halfx8 x, y;
+    __builtin_memcpy(&x, &a, sizeof(x));
+    __builtin_memcpy(&y, &b, sizeof(y));
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(x, y, c, 0, 0, 0);
+  } else {
+    bf16x8 x, y;
+    __builtin_memcpy(&x, &a, sizeof(x));
+    __builtin_memcpy(&y, &b, sizeof(y));
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c, 0, 0, 0);
+  }
 }
 
-template <class Epi>
-__global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<Epi> P) {
+// C_i = A_i Bt_i^T for 16-bit (bf16 or fp16) row-major stacks, fp32 accumulate.
+template <class Epi, int FMT>
+__global__ void __launch_bounds__(256, 2) gemm_h16_nt_kernel(const H16Launch<Epi> P) {
   constexpr int BM = 128, BN = 128, TM = 2, TN = 2;
-  constexpr int kTile = BM * kLd16;  // bf16 elements of one operand tile
+  constexpr int kTile = BM * kLd16;  // 16-bit elements of one operand tile
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * kTile];
 
   const uint32_t lid = xcd_remap(blockIdx.x, P.total);
-  const int64_t item = lid / P.tiles_per_item;
-  int t = lid - (uint32_t)item * P.tiles_per_item;
+  const uint32_t per_job = (uint32_t)P.nitems * P.tiles_per_item;
+  const int job = lid / per_job;
+  const uint32_t rem = lid - job * per_job;
+  const int64_t item = rem / P.tiles_per_item;
+  int t = rem - (uint32_t)item * P.tiles_per_item;
   int tm, tn;
   if (!P.sym) {
     tm = t / P.tiles_n;
@@ -77,8 +93,8 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<E
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int64_t off = item * (int64_t)P.B * P.B;
-  const uint16_t* A = P.a + off;
-  const uint16_t* Bt = P.bt + off;
+  const uint16_t* A = P.a[job] + off;
+  const uint16_t* Bt = P.bt[job] + off;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -122,25 +138,23 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<E
     if (s + 1 < nstages) gload((s + 1) * kBK16);
 #pragma unroll
     for (int ks = 0; ks < kBK16 / 16; ++ks) {
-      bf16x8 fa[TM], fb[TN];
+      u32x4 fa[TM], fb[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        fa[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(cur + (wm + 32 * i + rr) * kLd16 + ks * 16 + h * 8));
+        fa[i] = *reinterpret_cast<const u32x4*>(cur + (wm + 32 * i + rr) * kLd16 + ks * 16 + h * 8);
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        fb[j] = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(cur + kTile + (wn + 32 * j + rr) * kLd16 + ks * 16 + h * 8));
+        fb[j] = *reinterpret_cast<const u32x4*>(cur + kTile + (wn + 32 * j + rr) * kLd16 + ks * 16 + h * 8);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_h16<FMT>(fa[i], fb[j], acc[i][j]);
     }
     if (s + 1 < nstages) sstore(lds + ((s + 1) & 1) * 2 * kTile);
     __syncthreads();
   }
 
-  typename Epi::Tile tile(P.e, item, P.B);
+  typename Epi::Tile tile(P.e[job], item, P.B);
   if constexpr (Epi::kSym) {
     static_assert(sizeof(lds) >= sizeof(float) * BM * (BN + 1), "LDS too small for the transpose");
     if (P.sym) {
@@ -148,6 +162,7 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<E
       return;
     }
   }
+  float part = 0.f;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -156,8 +171,13 @@ __global__ void __launch_bounds__(256, 2) gemm_bf16_nt_kernel(const Bf16Launch<E
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
         const int col = n0 + wn + 32 * j + rr;
-        tile.store(row, col, acc[i][j][e]);
+        part += tile.store(row, col, acc[i][j][e]);
       }
+  if constexpr (Epi::kReduce) {
+    __shared__ float red[4];
+    const float tot = block_sum<256>(part, red);
+    if (threadIdx.x == 0) tile.partial(tm * P.tiles_n + tn, tot);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -249,25 +269,38 @@ static inline int bf16_gather(const shampoo_block* d, int64_t n, int B, uint16_t
   return bf16_cast_launch(o, g16, gt16, n, B, st);
 }
 
+// One launch of up to two NT products of 16-bit stacks with the same epilogue type.
 template <class Epi>
-static inline int bf16_gemm_nt(const uint16_t* a, const uint16_t* bt, const typename Epi::Job& e, int64_t n,
-                               int B, bool sym, hipStream_t st) {
+static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* bt, const typename Epi::Job* e,
+                              int njobs, int64_t n, int B, bool sym, int fmt, hipStream_t st) {
   if (B % 128 != 0) return SHAMPOO_EUNSUPPORTED;
-  Bf16Launch<Epi> P;
-  P.a = a;
-  P.bt = bt;
-  P.e = e;
+  H16Launch<Epi> P;
+  memset(&P, 0, sizeof(P));
+  for (int j = 0; j < njobs; ++j) {
+    P.a[j] = a[j];
+    P.bt[j] = bt[j];
+    P.e[j] = e[j];
+  }
   P.nitems = n;
   P.B = B;
   P.tiles_n = B / 128;
   P.tiles_per_item = sym ? P.tiles_n * (P.tiles_n + 1) / 2 : P.tiles_n * P.tiles_n;
   P.sym = sym ? 1 : 0;
-  const uint64_t total = (uint64_t)n * P.tiles_per_item;
+  const uint64_t total = (uint64_t)njobs * n * P.tiles_per_item;
   if (total == 0) return SHAMPOO_OK;
   if (total > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
   P.total = (uint32_t)total;
-  hipLaunchKernelGGL(gemm_bf16_nt_kernel<Epi>, dim3(P.total), dim3(256), 0, st, P);
+  if (fmt == H16_F16)
+    hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16>), dim3(P.total), dim3(256), 0, st, P);
+  else
+    hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_BF16>), dim3(P.total), dim3(256), 0, st, P);
   return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMPOO_EHIP;
+}
+
+template <class Epi>
+static inline int bf16_gemm_nt(const uint16_t* a, const uint16_t* bt, const typename Epi::Job& e, int64_t n,
+                               int B, bool sym, hipStream_t st) {
+  return h16_gemm_nt<Epi>(&a, &bt, &e, 1, n, B, sym, H16_BF16, st);
 }
 
 static inline int bf16_gemm_nt_store(const uint16_t* a, const uint16_t* bt, const EpiStore::Job& e, int64_t n,

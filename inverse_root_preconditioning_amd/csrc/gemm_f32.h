@@ -336,23 +336,29 @@ struct EpiStore {
   static constexpr bool kReduce = false;
   static constexpr bool kSym = true;
   struct Job {
-    float* out;
+    float* out;          // fp32 output (may be null when only the 16-bit copy is needed)
     const float* cin;
     float alpha, beta;
     const shampoo_scale* scale;
     const int32_t* status;
     float pexp, extra;
+    uint16_t* out16;     // optional 16-bit copy of the output (operand of a later product)
+    int fmt16;           // H16_BF16 or H16_F16
   };
   struct Tile {
     float* out;
     const float* cin;
+    uint16_t* o16;
+    int fmt;
     float mult, beta;
     bool ident;
     int B;
     __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
       const int64_t off = item * (int64_t)B_ * B_;
-      out = j.out + off;
+      out = j.out ? j.out + off : nullptr;
       cin = j.cin ? j.cin + off : nullptr;
+      o16 = j.out16 ? j.out16 + off : nullptr;
+      fmt = j.fmt16;
       beta = j.beta;
       mult = j.alpha;
       if (j.scale) mult *= j.extra * powf(safe_c(j.scale, j.status, item), j.pexp);
@@ -364,7 +370,11 @@ struct EpiStore {
       if (ident) o = (row == col) ? 1.f : 0.f;
       return o;
     }
-    __device__ __forceinline__ void write(int row, int col, float o) { stg(out + (int64_t)row * B + col, o); }
+    __device__ __forceinline__ void write(int row, int col, float o) {
+      const int64_t idx = (int64_t)row * B + col;
+      if (out) stg(out + idx, o);
+      if (o16) stg(o16 + idx, to_h16(o, fmt));
+    }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));
       return 0.f;
@@ -438,8 +448,11 @@ struct EpiCnM {
   static constexpr bool kSym = false;
   static constexpr bool kReduce = true;
   struct Job {
-    float* m;
+    float* m;            // fp32 outputs (null: not written)
     float* c;
+    uint16_t* m16;       // 16-bit copies (null: not written)
+    uint16_t* c16;
+    int fmt16;
     float* partials;
     int tiles;
     float p;
@@ -447,13 +460,19 @@ struct EpiCnM {
   struct Tile {
     float* m;
     float* c;
+    uint16_t* m16;
+    uint16_t* c16;
+    int fmt;
     float* part;
     float p1, pinv;
     int B;
     __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
       const int64_t off = item * (int64_t)B_ * B_;
-      m = j.m + off;
-      c = j.c + off;
+      m = j.m ? j.m + off : nullptr;
+      c = j.c ? j.c + off : nullptr;
+      m16 = j.m16 ? j.m16 + off : nullptr;
+      c16 = j.c16 ? j.c16 + off : nullptr;
+      fmt = j.fmt16;
       part = j.partials + item * j.tiles;
       p1 = j.p + 1.f;
       pinv = 1.f / j.p;
@@ -461,8 +480,11 @@ struct EpiCnM {
     __device__ __forceinline__ float store(int row, int col, float v) {
       const int64_t idx = (int64_t)row * B + col;
       const float d = (row == col) ? 1.f : 0.f;
-      stg(m + idx, v);
-      stg(c + idx, (p1 * d - v) * pinv);
+      const float cv = (p1 * d - v) * pinv;
+      if (m) stg(m + idx, v);
+      if (c) stg(c + idx, cv);
+      if (m16) stg(m16 + idx, to_h16(v, fmt));
+      if (c16) stg(c16 + idx, to_h16(cv, fmt));
       const float r = d - v;
       return r * r;
     }
@@ -473,13 +495,14 @@ struct EpiCnM {
 // Clenshaw step with T = 2 A_s - I applied in the epilogue (acc = A_s b1):
 //   b = cj I + 4 acc - 2 b1 - b2                        (final == 0)
 //   X = mult (cj I + 2 acc - b1 - b2), I if degenerate   (final == 1, cj = c_0)
-// An optional bf16 copy of b is written for the next bf16 product.
+// An optional 16-bit copy of b is written for the next half-width product.
 struct EpiClenshaw {
   static constexpr bool kReduce = false;
   static constexpr bool kSym = true;
   struct Job {
     float* out;
-    uint16_t* out_bf16;
+    uint16_t* out16;     // optional 16-bit copy of b (operand of the next product)
+    int fmt16;
     const float* b1;
     const float* b2;
     float cj;
@@ -491,6 +514,7 @@ struct EpiClenshaw {
   struct Tile {
     float* out;
     uint16_t* obf;
+    int fmt;
     const float* b1;
     const float* b2;
     float cj, mult, k1, k2;
@@ -499,7 +523,8 @@ struct EpiClenshaw {
     __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
       const int64_t off = item * (int64_t)B_ * B_;
       out = j.out + off;
-      obf = j.out_bf16 ? j.out_bf16 + off : nullptr;
+      obf = j.out16 ? j.out16 + off : nullptr;
+      fmt = j.fmt16;
       b1 = j.b1 + off;
       b2 = j.b2 + off;
       cj = j.cj;
@@ -525,7 +550,7 @@ struct EpiClenshaw {
     __device__ __forceinline__ void write(int row, int col, float o) {
       const int64_t idx = (int64_t)row * B + col;
       stg(out + idx, o);
-      if (obf) stg(obf + idx, f32_to_bf16_bits(o));
+      if (obf) stg(obf + idx, to_h16(o, fmt));
     }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));

@@ -270,7 +270,8 @@ enum {
   EW_CN_START = 1,    // m = a x + b I, c = ((p+1) I - m) / p, sum (I - m)^2
   EW_CHEBY_START = 2, // as = a x + b I, bd = cd I, bd1 = cd1 I + 2 cd (2 as - I)
   EW_SCALE_COPY = 3,  // out = mult x (mult = extra c^pexp), I if degenerate
-  EW_CHEBY_LINEAR = 4 // out = mult (c0 I + c1 (2 (a x + b I) - I)), I if degenerate
+  EW_CHEBY_LINEAR = 4, // out = mult (c0 I + c1 (2 (a x + b I) - I)), I if degenerate
+  EW_CN16_START = 5   // as EW_CN_START, m and c written only as 16-bit copies (h0, h1)
 };
 
 struct EwArgs {
@@ -285,6 +286,9 @@ struct EwArgs {
   float p;                     // root order
   float c0, c1;                // Chebyshev coefficients (c_d, c_{d-1} or c_0, c_1)
   float pexp, extra;           // scale copy: mult = extra c^pexp
+  uint16_t* h0;                // 16-bit outputs (EW_CN16_START)
+  uint16_t* h1;
+  int fmt16;
   int B;
   int chunks;                  // workgroups per item
 };
@@ -337,7 +341,7 @@ __global__ void __launch_bounds__(256) ew_kernel(const EwArgs P) {
         o0[e] = y;
         o1[e] = 1.5f * d - 0.5f * y;
         part += (d - y) * (d - y);
-      } else if (MODE == EW_CN_START) {
+      } else if (MODE == EW_CN_START || MODE == EW_CN16_START) {
         o0[e] = y;
         o1[e] = (p1 * d - y) * pinv;
         part += (d - y) * (d - y);
@@ -351,7 +355,16 @@ __global__ void __launch_bounds__(256) ew_kernel(const EwArgs P) {
         o0[e] = ident ? d : mult * (P.c0 * d + P.c1 * (2.f * y - d));
       }
     }
-    if (P.out0) stg(reinterpret_cast<floatx4*>(P.out0 + off + 4 * i), o0);
+    if (MODE == EW_CN16_START) {
+      u32x2 w0, w1;
+      w0.x = (uint32_t)to_h16(o0[0], P.fmt16) | ((uint32_t)to_h16(o0[1], P.fmt16) << 16);
+      w0.y = (uint32_t)to_h16(o0[2], P.fmt16) | ((uint32_t)to_h16(o0[3], P.fmt16) << 16);
+      w1.x = (uint32_t)to_h16(o1[0], P.fmt16) | ((uint32_t)to_h16(o1[1], P.fmt16) << 16);
+      w1.y = (uint32_t)to_h16(o1[2], P.fmt16) | ((uint32_t)to_h16(o1[3], P.fmt16) << 16);
+      stg(reinterpret_cast<u32x2*>(P.h0 + off + 4 * i), w0);
+      stg(reinterpret_cast<u32x2*>(P.h1 + off + 4 * i), w1);
+    }
+    if (P.out0 && MODE != EW_CN16_START) stg(reinterpret_cast<floatx4*>(P.out0 + off + 4 * i), o0);
     if (MODE == EW_NDB_START || MODE == EW_CN_START || MODE == EW_CHEBY_START)
       stg(reinterpret_cast<floatx4*>(P.out1 + off + 4 * i), o1);
     if (MODE == EW_CHEBY_START) stg(reinterpret_cast<floatx4*>(P.out2 + off + 4 * i), o2);

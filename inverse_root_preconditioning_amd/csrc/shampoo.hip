@@ -171,7 +171,47 @@ struct NewtonWs {
   float* partials;
 };
 
+// A pool of 16-bit stacks for the half-width coupled Newton.
+struct Pool16 {
+  uint16_t* buf[8];
+  bool used[8];
+  int n = 0;
+  uint16_t* get() {
+    for (int i = 0; i < n; ++i)
+      if (!used[i]) {
+        used[i] = true;
+        return buf[i];
+      }
+    return nullptr;
+  }
+  void put(uint16_t* p) {
+    for (int i = 0; i < n; ++i)
+      if (buf[i] == p) used[i] = false;
+  }
+};
+
+struct Cn16Ws {
+  Pool16 pool;
+  float* c32;       // fp32 C_0 (one iteration only)
+  float* partials;
+};
+
+size_t cn16_layout(Carver& c, int64_t nf, int B, Cn16Ws* out) {
+  Cn16Ws w;
+  w.c32 = c.take<float>(stack_elems(nf, B));
+  w.pool.n = 7;
+  for (int i = 0; i < 7; ++i) {
+    w.pool.buf[i] = c.take<uint16_t>(stack_elems(nf, B));
+    w.pool.used[i] = false;
+  }
+  const int cnt = gemm_tiles(B) > ew_chunks(B) ? gemm_tiles(B) : ew_chunks(B);
+  w.partials = c.take<float>((size_t)nf * cnt);
+  if (out) *out = w;
+  return c.off;
+}
+
 size_t newton_layout(Carver& c, int64_t nf, int B, int variant, NewtonWs* out) {
+  if (variant == SHAMPOO_CN_F16) return cn16_layout(c, nf, B, nullptr);
   const int nbuf = (variant == SHAMPOO_CN) ? 7 : 5;
   NewtonWs w;
   w.pool.n = nbuf;
@@ -294,6 +334,8 @@ struct FinalOut {
 
 EpiStore::Job final_job(const FinalOut& fo) {
   EpiStore::Job j;
+  j.out16 = nullptr;
+  j.fmt16 = H16_BF16;
   j.out = fo.x;
   j.cin = nullptr;
   j.alpha = 1.f;
@@ -305,8 +347,10 @@ EpiStore::Job final_job(const FinalOut& fo) {
   return j;
 }
 
-EpiStore::Job plain_job(float* out) {
+EpiStore::Job plain_job(float* out, uint16_t* out16 = nullptr, int fmt16 = H16_BF16) {
   EpiStore::Job j;
+  j.out16 = out16;
+  j.fmt16 = fmt16;
   j.out = out;
   j.cin = nullptr;
   j.alpha = 1.f;
@@ -582,12 +626,153 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
       EpiCnM::Job j;
       j.m = Mn;
       j.c = Cn;
+      j.m16 = nullptr;
+      j.c16 = nullptr;
+      j.fmt16 = H16_BF16;
       j.partials = ws->partials;
       j.tiles = tiles;
       j.p = (float)p;
       const float* A[1] = {Cp};
       const float* Bm[1] = {M};
-      SHP_TRY(gemm_nn<EpiCnM>(A, Bm, &j, 1, nf, B, st));
+      SHP_TRY(gemm_nn<EpiCnM>(A, Bm, &j, 1, nf, B, st, false, SHAMPOO_TIME_CN_M));
+      SHP_TRY(run_resid(ws->partials, tiles, resid, iters, it + 1, status, nf, st));
+    }
+    if (Cp != C) pool.put(Cp);
+    pool.put(M);
+    if (it > 0) {
+      pool.put(X);
+      pool.put(C);
+      X = Xn;
+    }
+    M = Mn;
+    C = Cn;
+  }
+  return SHAMPOO_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Coupled Newton on fp16 operands (fp32 accumulate).  Only 16-bit copies of
+// the iterates are kept; the final product writes X in fp32.  Every product
+// is in NT form with the row-major fp16 copy of the right operand standing
+// for its transpose: C, C^2, C^4 and M are polynomials in A_s, symmetric in
+// exact arithmetic, and their rounding asymmetry is far below fp16 precision.
+// ---------------------------------------------------------------------------
+int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, int iters, float* x,
+                       float* resid, int32_t* status, Cn16Ws* ws, hipStream_t st, bool sym) {
+  const float pexp = -1.f / (float)p;
+  if (iters == 1) {  // X_1 = C_0: no product
+    EwArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = F;
+    a.out1 = ws->c32;
+    a.partials = ws->partials;
+    a.sc = sc;
+    a.status = status;
+    a.p = (float)p;
+    a.B = B;
+    a.chunks = ew_chunks(B);
+    SHP_TRY(run_ew<EW_CN_START>(a, nf, st));
+    SHP_TRY(run_resid(ws->partials, a.chunks, resid, 1, 0, status, nf, st));
+    EwArgs s2;
+    memset(&s2, 0, sizeof(s2));
+    s2.x = ws->c32;
+    s2.out0 = x;
+    s2.sc = sc;
+    s2.status = status;
+    s2.pexp = pexp;
+    s2.extra = 1.f;
+    s2.p = 1.f;
+    s2.B = B;
+    s2.chunks = ew_chunks(B);
+    return run_ew<EW_SCALE_COPY>(s2, nf, st);
+  }
+  Pool16& pool = ws->pool;
+  uint16_t* M = pool.get();
+  uint16_t* C = pool.get();
+  if (M == nullptr || C == nullptr) return SHAMPOO_EWORKSPACE;
+  {
+    EwArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = F;
+    a.h0 = M;
+    a.h1 = C;
+    a.fmt16 = H16_F16;
+    a.partials = ws->partials;
+    a.sc = sc;
+    a.status = status;
+    a.p = (float)p;
+    a.B = B;
+    a.chunks = ew_chunks(B);
+    SHP_TRY(run_ew<EW_CN16_START>(a, nf, st));
+    SHP_TRY(run_resid(ws->partials, a.chunks, resid, iters, 0, status, nf, st));
+  }
+  const int tiles = gemm_tiles(B);
+  uint16_t* X = nullptr;
+  for (int it = 0; it < iters; ++it) {
+    if (it == iters - 1) {
+      FinalOut fo{x, sc, status, pexp, 1.f};
+      EpiStore::Job j = final_job(fo);
+      const uint16_t* A[1] = {X};
+      const uint16_t* Bt[1] = {C};
+      return h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st);
+    }
+    if (it == 0) X = C;  // X_1 = C_0; the buffer now belongs to X
+    uint16_t* Cp = C;
+    uint16_t* Xn = nullptr;
+    if (p >= 2) {
+      uint16_t* C2 = pool.get();
+      if (C2 == nullptr) return SHAMPOO_EWORKSPACE;
+      if (it > 0) {
+        Xn = pool.get();
+        if (Xn == nullptr) return SHAMPOO_EWORKSPACE;
+        EpiStore::Job j[2] = {plain_job(nullptr, Xn, H16_F16), plain_job(nullptr, C2, H16_F16)};
+        const uint16_t* A[2] = {X, C};
+        const uint16_t* Bt[2] = {C, C};
+        SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, j, 2, nf, B, sym, H16_F16, st));
+      } else {
+        EpiStore::Job j = plain_job(nullptr, C2, H16_F16);
+        const uint16_t* A[1] = {C};
+        const uint16_t* Bt[1] = {C};
+        SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st));
+      }
+      Cp = C2;
+      for (int q = 4; q <= p; q *= 2) {
+        uint16_t* Cq = pool.get();
+        if (Cq == nullptr) return SHAMPOO_EWORKSPACE;
+        EpiStore::Job j = plain_job(nullptr, Cq, H16_F16);
+        const uint16_t* A[1] = {Cp};
+        const uint16_t* Bt[1] = {Cp};
+        SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st));
+        pool.put(Cp);
+        Cp = Cq;
+      }
+    } else if (it > 0) {
+      Xn = pool.get();
+      if (Xn == nullptr) return SHAMPOO_EWORKSPACE;
+      EpiStore::Job j = plain_job(nullptr, Xn, H16_F16);
+      const uint16_t* A[1] = {X};
+      const uint16_t* Bt[1] = {C};
+      SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st));
+    }
+    uint16_t* Mn = pool.get();
+    uint16_t* Cn = pool.get();
+    if (Mn == nullptr || Cn == nullptr) return SHAMPOO_EWORKSPACE;
+    {
+      EpiCnM::Job j;
+      j.m = nullptr;
+      j.c = nullptr;
+      j.m16 = Mn;
+      j.c16 = Cn;
+      j.fmt16 = H16_F16;
+      j.partials = ws->partials;
+      j.tiles = tiles;
+      j.p = (float)p;
+      const uint16_t* A[1] = {Cp};
+      const uint16_t* Bt[1] = {M};
+      timing_before(SHAMPOO_TIME_CN_M, st);
+      const int rc = h16_gemm_nt<EpiCnM>(A, Bt, &j, 1, nf, B, false, H16_F16, st);
+      timing_after(SHAMPOO_TIME_CN_M, st);
+      SHP_TRY(rc);
       SHP_TRY(run_resid(ws->partials, tiles, resid, iters, it + 1, status, nf, st));
     }
     if (Cp != C) pool.put(Cp);
@@ -660,7 +845,8 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
   for (int j = degree - 2; j >= 0; --j) {
     EpiClenshaw::Job e;
     e.out = (j == 0) ? x : ws->b[i0];
-    e.out_bf16 = (bf && j > 0) ? ws->b16[s1 ^ 1] : nullptr;
+    e.out16 = (bf && j > 0) ? ws->b16[s1 ^ 1] : nullptr;
+    e.fmt16 = H16_BF16;
     e.b1 = ws->b[i1];
     e.b2 = ws->b[i2];
     e.cj = (float)c[j];
@@ -697,7 +883,7 @@ extern "C" {
 int shampoo_abi_version(void) { return SHAMPOO_ABI_VERSION; }
 
 int shampoo_timing_hook(int family, hipEvent_t* events, int capacity) {
-  if (family < 0 || family > SHAMPOO_TIME_CLENSHAW || capacity < 0) return SHAMPOO_EINVAL;
+  if (family < 0 || family > SHAMPOO_TIME_CN_M || capacity < 0) return SHAMPOO_EINVAL;
   if (family != 0 && (events == nullptr || capacity == 0)) return SHAMPOO_EINVAL;
   g_timing.family = family;
   g_timing.events = family ? events : nullptr;
@@ -729,7 +915,7 @@ size_t shampoo_workspace_bytes(int op, int64_t count, int B, int variant_or_degr
     case SHAMPOO_OP_ACCUMULATE: return accum_layout(c, count, B, prec, nullptr);
     case SHAMPOO_OP_SCALE: return scale_layout(c, count, B, nullptr);
     case SHAMPOO_OP_NEWTON:
-      if (variant_or_degree < SHAMPOO_NDB || variant_or_degree > SHAMPOO_CN) return 0;
+      if (variant_or_degree < SHAMPOO_NDB || variant_or_degree > SHAMPOO_CN_F16) return 0;
       return newton_layout(c, count, B, variant_or_degree, nullptr);
     case SHAMPOO_OP_CHEBY: return cheby_layout(c, count, B, prec, nullptr);
     case SHAMPOO_OP_PRECONDITION: return precond_layout(c, count, B, prec, nullptr);
@@ -755,6 +941,8 @@ int shampoo_accumulate(const shampoo_block* g_blocks, int64_t nblocks, int B, fl
   accum_layout(c, nblocks, B, prec, &w);
 
   EpiStore::Job jl;
+  jl.out16 = nullptr;
+  jl.fmt16 = H16_BF16;
   jl.out = factors;
   jl.cin = factors;
   jl.alpha = gamma;
@@ -846,19 +1034,25 @@ int shampoo_invroot_newton(const float* factors, const shampoo_scale* scale, int
   variant &= ~SHAMPOO_FULL_PRODUCTS;
   if (nfactors < 0) return SHAMPOO_EINVAL;
   if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
-  if (variant < SHAMPOO_NDB || variant > SHAMPOO_CN) return SHAMPOO_EINVAL;
+  if (variant < SHAMPOO_NDB || variant > SHAMPOO_CN_F16) return SHAMPOO_EINVAL;
   if (iters < 1 || iters > 100) return SHAMPOO_EINVAL;
-  if (variant == SHAMPOO_CN) {
+  if (variant == SHAMPOO_CN || variant == SHAMPOO_CN_F16) {
     if (p != 1 && p != 2 && p != 4 && p != 8) return SHAMPOO_EUNSUPPORTED;
   } else if (p != 2 && p != 4) {
     return SHAMPOO_EUNSUPPORTED;
   }
+  if (variant == SHAMPOO_CN_F16 && (B % 128) != 0) return SHAMPOO_EUNSUPPORTED;
   if (nfactors == 0) return SHAMPOO_OK;
   if (factors == nullptr || scale == nullptr || x_out == nullptr || status == nullptr) return SHAMPOO_EINVAL;
   Carver cm(nullptr);
   const size_t need = newton_layout(cm, nfactors, B, variant, nullptr);
   if (ws == nullptr || ws_bytes < need) return SHAMPOO_EWORKSPACE;
   Carver c(ws);
+  if (variant == SHAMPOO_CN_F16) {
+    Cn16Ws w16;
+    cn16_layout(c, nfactors, B, &w16);
+    return coupled_newton_h16(factors, scale, nfactors, B, p, iters, x_out, resid_out, status, &w16, stream, sym);
+  }
   NewtonWs w;
   newton_layout(c, nfactors, B, variant, &w);
   if (variant == SHAMPOO_CN)

@@ -53,7 +53,7 @@ def gpu_roots(F, sc, st, method, iters=10, p=4, variant=capi.NDB, degree=24, del
     R = None
     if method == "newton":
         if resid:
-            passes = 1 if (p == 2 or (variant & ~capi.FULL_PRODUCTS) == capi.CN) else 2
+            passes = 1 if (p == 2 or (variant & ~capi.FULL_PRODUCTS) in (capi.CN, capi.CN_F16)) else 2
             R = torch.full((F.shape[0], passes * iters), -1.0, dtype=torch.float32, device=F.device)
         PL.invroot_newton(F, sc, p, variant, iters, X, st, R)
     else:
@@ -61,8 +61,8 @@ def gpu_roots(F, sc, st, method, iters=10, p=4, variant=capi.NDB, degree=24, del
     return X, R
 
 
-VARIANT_NAME = {capi.NDB: "ndb", capi.NDB_Z: "ndb", capi.CN: "cn"}
-CHAINING = {capi.NDB: "Y", capi.NDB_Z: "Z", capi.CN: "Y"}
+VARIANT_NAME = {capi.NDB: "ndb", capi.NDB_Z: "ndb", capi.CN: "cn", capi.CN_F16: "cn"}
+CHAINING = {capi.NDB: "Y", capi.NDB_Z: "Z", capi.CN: "Y", capi.CN_F16: "Y"}
 
 
 def oracle_scale(F, eps_rel, mode, V0, steps=20, safety=2.0):

@@ -59,6 +59,7 @@ def test_workspace_sizes():
     stack = nf * B * B * 4
     assert ws(capi.OP_NEWTON, nf, B, capi.NDB, capi.F32) >= 5 * stack
     assert ws(capi.OP_NEWTON, nf, B, capi.CN, capi.F32) >= 7 * stack
+    assert ws(capi.OP_NEWTON, nf, B, capi.CN_F16, capi.F32) >= stack + 7 * stack // 2
     assert ws(capi.OP_CHEBY, nf, B, 16, capi.F32) >= 4 * stack
     assert ws(capi.OP_CHEBY, nf, B, 16, capi.BF16_IN) > ws(capi.OP_CHEBY, nf, B, 16, capi.F32)
     assert ws(capi.OP_SCALE, nf, B, 0, capi.F32) >= 2 * nf * B * 32 * 4
@@ -83,6 +84,8 @@ def test_validation_codes_without_gpu():
     assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 64, 3, f.NDB, 5, FAKE, 0, FAKE, FAKE, 1 << 40, 0) == f.EUNSUPPORTED
     assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 64, 3, f.CN, 5, FAKE, 0, FAKE, FAKE, 1 << 40, 0) == f.EUNSUPPORTED
     assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 64, 4, 9, 5, FAKE, 0, FAKE, FAKE, 1 << 40, 0) == f.EINVAL
+    assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 192, 4, f.CN_F16, 5, FAKE, 0, FAKE, FAKE, 1 << 40, 0) == f.EUNSUPPORTED
+    assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 256, 3, f.CN_F16, 5, FAKE, 0, FAKE, FAKE, 1 << 40, 0) == f.EUNSUPPORTED
     # null pointers and workspace
     assert f.shampoo_invroot_newton(0, FAKE, 4, 64, 4, f.NDB, 5, FAKE, 0, FAKE, FAKE, 1 << 40, 0) == f.EINVAL
     assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 64, 4, f.NDB, 5, FAKE, 0, FAKE, FAKE, 16, 0) == f.EWORKSPACE

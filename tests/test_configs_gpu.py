@@ -233,6 +233,16 @@ def test_config3_sampled(variant):
 
 
 @pytest.mark.slow
+def test_config3_sampled_coupled_newton_fp16():
+    """The pages' fastest configuration (coupled Newton in FP16) on the 360M-shaped step."""
+    B = 1024
+    run = model_step(3, W.MODEL_360M, B, "newton", variant=capi.CN_F16)
+    picks, ef, ex, eu = sampled_parity(3, *run, B, "newton", capi.CN, 24, 10)
+    report("config3_cn_fp16", blocks=picks, factor_err=ef, root_err=ex, U_err=eu)
+    assert ef <= 1e-5 and ex <= TOL_BF16 and eu <= TOL_BF16
+
+
+@pytest.mark.slow
 def test_config5_sampled_bf16_chebyshev():
     B = 2048
     run = model_step(5, W.MODEL_1_3B, B, "cheby", prec=capi.BF16_IN, degree=24)

@@ -300,3 +300,27 @@ def test_repeat_runs_are_bitwise_identical():
         outs.append((host(sc), host(X), host(R)))
     for a, b in zip(outs[0], outs[1]):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("full", [False, True])
+@pytest.mark.parametrize("B", [128, 256])
+@pytest.mark.parametrize("p,iters", [(4, 1), (4, 2), (4, 6), (4, 12), (1, 6), (2, 6), (8, 6)])
+def test_coupled_newton_fp16_matches_oracle(B, p, iters, full):
+    """Coupled Newton on fp16 operands with fp32 accumulation, against the
+    float64 coupled Newton (half-width-input tolerance 2e-2)."""
+    nf = 4
+    F = W.spd_factors(130 + B, nf, B, cond=1e3)
+    V0 = W.start_vectors(131, nf, B)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    v = capi.CN_F16 | (capi.FULL_PRODUCTS if full else 0)
+    X, R = gpu_roots(Fd, sc, st, "newton", iters=iters, p=p, variant=v, resid=True)
+    Xh, Rh = host(X), host(R)
+    err = 0.0
+    for i in range(nf):
+        o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
+        err = max(err, O.relative_frobenius(Xh[i], oracle_root(F[i], o, "newton", iters=iters, p=p,
+                                                                variant=capi.CN)))
+    assert err <= TOL_BF16, err
+    assert np.all(np.isfinite(Rh)) and np.all(Rh >= 0.0)
+    report("cn_fp16", B=B, p=p, iters=iters, full=full, err=err)
