@@ -6,7 +6,8 @@
 // row-major 16-bit stacks, so both operands are read along k with 16-byte
 // loads.  Operands that are needed transposed are produced transposed by
 // the cast kernels (or by the epilogue of the previous step).  Tiles are
-// 128 x 128 per workgroup (4 waves of 64 x 64), k staged 64 at a time.
+// 256 x 256 per workgroup for full products when B % 256 == 0, else 128 x
+// 128; k is staged 64 at a time.
 #pragma once
 
 #include "gemm_f32.h"
@@ -64,12 +65,104 @@ __device__ __forceinline__ floatx16 mfma_h16(const u32x4& a, const u32x4& b, con
   }
 }
 
+// Epilogue through LDS for workgroups with many accumulators: in each of PH
+// phases the waves whose rows fall in it stage their raw accumulators, then
+// all NT threads apply the epilogue in row-major order (consecutive threads,
+// consecutive columns), so no accumulator register is live while the
+// epilogue's own loads are in flight.  For a symmetric product (`sym`) the
+// value formed at each computed position is written there (on a diagonal
+// tile only on and above the diagonal), kept in LDS, and written mirrored
+// through a transposed pass.  `lds` needs (BM / PH) x (BN + 1) floats and
+// must be free.  Returns this thread's share of the tile's reduction.
+template <int TM, int TN, int BM, int BN, int NT, int PH, class Epi>
+__device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, floatx16 (&acc)[TM][TN], float* lds,
+                                                 int m0, int n0, int wm, int wn, int lane, bool sym, bool diag) {
+  constexpr int LD = BN + 1, RH = BM / PH;
+  static_assert(RH % (32 * TM) == 0, "a wave's rows must fall in one phase");
+  float part = 0.f;
+#pragma unroll
+  for (int h = 0; h < PH; ++h) {
+    if (PH == 1 || wm / RH == h) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int rl = wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int cl = wn + 32 * j + (lane & 31);
+            lds[(rl - h * RH) * LD + cl] = acc[i][j][e];
+          }
+    }
+    __syncthreads();
+    const int r0 = m0 + h * RH;
+    if constexpr (Epi::kSym) {
+      if (sym) {
+        for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
+          const int b = idx / BN, a = idx - (idx / BN) * BN;
+          const float o = tile.value(r0 + b, n0 + a, lds[b * LD + a]);
+          if (!diag || r0 + b <= n0 + a) tile.write(r0 + b, n0 + a, o);
+          lds[b * LD + a] = o;
+        }
+        __syncthreads();
+        // o[b][a] goes to (n0 + a, r0 + b); on a diagonal tile only from above the diagonal.
+        for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
+          const int a = idx / RH, b = idx - (idx / RH) * RH;
+          if (!diag || n0 + a > r0 + b) tile.write(n0 + a, r0 + b, lds[b * LD + a]);
+        }
+        if (h + 1 < PH) __syncthreads();
+        continue;
+      }
+    }
+    for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
+      const int b = idx / BN, a = idx - (idx / BN) * BN;
+      part += tile.store(r0 + b, n0 + a, lds[b * LD + a]);
+    }
+    if (h + 1 < PH) __syncthreads();
+  }
+  return part;
+}
+
+// Workgroup shapes of the 16-bit product.  The LDS traffic per MFMA falls
+// with the wave tile: 64 x 64 wave tiles read 1 KB of fragments per 32 x 32 x 16
+// MFMA, 64 x 128 ones 0.75 KB, and the 256 x 256 workgroup tile halves the
+// staging writes per MFMA as well.
+//   H16_T128: 128 x 128 tiles, 4 waves of 64 x 64, two workgroups per CU.
+//   H16_T256: 256 x 256 tiles, 8 waves (4 x 2) of 64 x 128, one workgroup per
+//             CU (144 KB of LDS); full products with B % 256 == 0.
+enum { H16_T128 = 0, H16_T256 = 1 };
+
+template <int CFG>
+struct H16Shape {
+  static constexpr int BM = CFG == H16_T256 ? 256 : 128;
+  static constexpr int WR = CFG == H16_T256 ? 4 : 2;   // waves along rows
+  static constexpr int WC = 2;                          // waves along columns
+  static constexpr int NT = 64 * WR * WC;
+  static constexpr int TM = BM / WR / 32, TN = BM / WC / 32;
+  static constexpr int MINW = CFG == H16_T256 ? 1 : 2;
+};
+
+// Symmetric products stay on 128 x 128 tiles: their diagonal tiles are
+// computed whole, which wastes more work on larger tiles, and their
+// epilogues (EMA and Clenshaw terms, mirrored writes) outweigh the main-loop
+// gain.
+__host__ __device__ constexpr int h16_tile_of(int B, bool sym) { return (!sym && B % 256 == 0) ? 256 : 128; }
+
 // C_i = A_i Bt_i^T for 16-bit (bf16 or fp16) row-major stacks, fp32 accumulate.
-template <class Epi, int FMT>
-__global__ void __launch_bounds__(256, 2) gemm_h16_nt_kernel(const H16Launch<Epi> P) {
-  constexpr int BM = 128, BN = 128, TM = 2, TN = 2;
-  constexpr int kTile = BM * kLd16;  // 16-bit elements of one operand tile
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * kTile];
+// k is staged kBK16 deep through two padded LDS buffers (loads of stage s + 1
+// are in registers while stage s is multiplied); the fragments of the next
+// 16-deep k step are read before the MFMAs of the current one, across the
+// stage boundary too.
+template <class Epi, int FMT, int CFG>
+__global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
+    gemm_h16_nt_kernel(const H16Launch<Epi> P) {
+  using S = H16Shape<CFG>;
+  constexpr int BM = S::BM, BN = S::BM, NT = S::NT, TM = S::TM, TN = S::TN, WC = S::WC;
+  constexpr int CPR = kBK16 / 8;          // 16-byte chunks per staged row
+  constexpr int LA = BM * CPR / NT;       // 16-byte loads per thread per operand and stage
+  constexpr int kA = BM * kLd16, kStage = 2 * kA;
+  constexpr int KS = kBK16 / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
 
   const uint32_t lid = xcd_remap(blockIdx.x, P.total);
   const uint32_t per_job = (uint32_t)P.nitems * P.tiles_per_item;
@@ -93,12 +186,14 @@ __global__ void __launch_bounds__(256, 2) gemm_h16_nt_kernel(const H16Launch<Epi
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int64_t off = item * (int64_t)P.B * P.B;
-  const uint16_t* A = P.a[job] + off;
-  const uint16_t* Bt = P.bt[job] + off;
+  // uniform selects, not an index into the argument arrays (which would put
+  // the arguments in scratch memory)
+  const uint16_t* A = (job == 0 ? P.a[0] : P.a[1]) + off;
+  const uint16_t* Bt = (job == 0 ? P.bt[0] : P.bt[1]) + off;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave / WC) * 32 * TM, wn = (wave % WC) * 32 * TN;
   const int rr = lane & 31, h = lane >> 5;
 
   floatx16 acc[TM][TN];
@@ -109,73 +204,99 @@ __global__ void __launch_bounds__(256, 2) gemm_h16_nt_kernel(const H16Launch<Epi
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  u32x4 ra[4], rb[4];
+  u32x4 ra[LA], rb[LA];
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = tid + 256 * it;
-      const int row = idx >> 3, ch = idx & 7;
+    for (int it = 0; it < LA; ++it) {
+      const int idx = tid + NT * it;
+      const int row = idx / CPR, ch = idx % CPR;
       ra[it] = ldg(reinterpret_cast<const u32x4*>(A + (int64_t)(m0 + row) * P.B + k0 + ch * 8));
       rb[it] = ldg(reinterpret_cast<const u32x4*>(Bt + (int64_t)(n0 + row) * P.B + k0 + ch * 8));
     }
   };
   auto sstore = [&](uint16_t* buf) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = tid + 256 * it;
-      const int row = idx >> 3, ch = idx & 7;
+    for (int it = 0; it < LA; ++it) {
+      const int idx = tid + NT * it;
+      const int row = idx / CPR, ch = idx % CPR;
       *reinterpret_cast<u32x4*>(buf + row * kLd16 + ch * 8) = ra[it];
-      *reinterpret_cast<u32x4*>(buf + kTile + row * kLd16 + ch * 8) = rb[it];
+      *reinterpret_cast<u32x4*>(buf + kA + row * kLd16 + ch * 8) = rb[it];
     }
+  };
+  auto frags = [&](const uint16_t* buf, int ks, u32x4(&fa)[TM], u32x4(&fb)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      fa[i] = *reinterpret_cast<const u32x4*>(buf + (wm + 32 * i + rr) * kLd16 + ks * 16 + h * 8);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      fb[j] = *reinterpret_cast<const u32x4*>(buf + kA + (wn + 32 * j + rr) * kLd16 + ks * 16 + h * 8);
   };
 
   const int nstages = P.B / kBK16;
   gload(0);
   sstore(lds);
   __syncthreads();
+  u32x4 ca[TM], cb[TN];
+  frags(lds, 0, ca, cb);
   for (int s = 0; s < nstages; ++s) {
-    const uint16_t* cur = lds + (s & 1) * 2 * kTile;
+    const uint16_t* cur = lds + (s & 1) * kStage;
     if (s + 1 < nstages) gload((s + 1) * kBK16);
 #pragma unroll
-    for (int ks = 0; ks < kBK16 / 16; ++ks) {
-      u32x4 fa[TM], fb[TN];
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 na[TM], nb[TN];
+      if (ks + 1 < KS) {
+        frags(cur, ks + 1, na, nb);
+      } else if (s + 1 < nstages) {
+        uint16_t* nxt = lds + ((s + 1) & 1) * kStage;
+        sstore(nxt);
+        __syncthreads();
+        frags(nxt, 0, na, nb);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        fa[i] = *reinterpret_cast<const u32x4*>(cur + (wm + 32 * i + rr) * kLd16 + ks * 16 + h * 8);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_h16<FMT>(ca[i], cb[j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ca[i] = na[i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) cb[j] = nb[j];
+    }
+  }
+  __syncthreads();  // the LDS is reused by the epilogue
+
+  typename Epi::Job job_args = P.e[0];
+  if (job != 0) job_args = P.e[1];
+  typename Epi::Tile tile(job_args, item, P.B);
+  float part = 0.f;
+  if constexpr (CFG == H16_T256) {
+    constexpr int PH = (sizeof(lds) >= sizeof(float) * BM * (BN + 1)) ? 1 : 2;
+    static_assert(sizeof(lds) >= sizeof(float) * (BM / PH) * (BN + 1), "LDS too small for the staging");
+    part = staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn,
+                                                        lane, P.sym != 0, tm == tn);
+  } else {
+    if constexpr (Epi::kSym) {
+      constexpr int PH = (sizeof(lds) >= sizeof(float) * BM * (BN + 1)) ? 1 : 2;
+      static_assert(sizeof(lds) >= sizeof(float) * (BM / PH) * (BN + 1), "LDS too small for the transpose");
+      if (P.sym) {
+        sym_epilogue<TM, TN, BM, BN, NT, PH>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, lane,
+                                             tm == tn);
+        return;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        fb[j] = *reinterpret_cast<const u32x4*>(cur + kTile + (wn + 32 * j + rr) * kLd16 + ks * 16 + h * 8);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_h16<FMT>(fa[i], fb[j], acc[i][j]);
-    }
-    if (s + 1 < nstages) sstore(lds + ((s + 1) & 1) * 2 * kTile);
-    __syncthreads();
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+          const int col = n0 + wn + 32 * j + rr;
+          part += tile.store(row, col, acc[i][j][e]);
+        }
   }
-
-  typename Epi::Tile tile(P.e[job], item, P.B);
-  if constexpr (Epi::kSym) {
-    static_assert(sizeof(lds) >= sizeof(float) * BM * (BN + 1), "LDS too small for the transpose");
-    if (P.sym) {
-      sym_epilogue<TM, TN, 1>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, lane, tm == tn);
-      return;
-    }
-  }
-  float part = 0.f;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-        const int col = n0 + wn + 32 * j + rr;
-        part += tile.store(row, col, acc[i][j][e]);
-      }
   if constexpr (Epi::kReduce) {
-    __shared__ float red[4];
-    const float tot = block_sum<256>(part, red);
+    __shared__ float red[NT / kWave];
+    const float tot = block_sum<NT>(part, red);
     if (threadIdx.x == 0) tile.partial(tm * P.tiles_n + tn, tot);
   }
 }
@@ -274,6 +395,7 @@ template <class Epi>
 static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* bt, const typename Epi::Job* e,
                               int njobs, int64_t n, int B, bool sym, int fmt, hipStream_t st) {
   if (B % 128 != 0) return SHAMPOO_EUNSUPPORTED;
+  const int T = h16_tile_of(B, sym);
   H16Launch<Epi> P;
   memset(&P, 0, sizeof(P));
   for (int j = 0; j < njobs; ++j) {
@@ -283,17 +405,26 @@ static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* b
   }
   P.nitems = n;
   P.B = B;
-  P.tiles_n = B / 128;
+  P.tiles_n = B / T;
   P.tiles_per_item = sym ? P.tiles_n * (P.tiles_n + 1) / 2 : P.tiles_n * P.tiles_n;
   P.sym = sym ? 1 : 0;
   const uint64_t total = (uint64_t)njobs * n * P.tiles_per_item;
   if (total == 0) return SHAMPOO_OK;
   if (total > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
   P.total = (uint32_t)total;
-  if (fmt == H16_F16)
-    hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16>), dim3(P.total), dim3(256), 0, st, P);
-  else
-    hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_BF16>), dim3(P.total), dim3(256), 0, st, P);
+  if (T == 256) {
+    constexpr int NT = H16Shape<H16_T256>::NT;
+    if (fmt == H16_F16)
+      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16, H16_T256>), dim3(P.total), dim3(NT), 0, st, P);
+    else
+      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_BF16, H16_T256>), dim3(P.total), dim3(NT), 0, st, P);
+  } else {
+    constexpr int NT = H16Shape<H16_T128>::NT;
+    if (fmt == H16_F16)
+      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16, H16_T128>), dim3(P.total), dim3(NT), 0, st, P);
+    else
+      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_BF16, H16_T128>), dim3(P.total), dim3(NT), 0, st, P);
+  }
   return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMPOO_EHIP;
 }
 

@@ -150,18 +150,20 @@ struct GemmLaunch {
 // Each lane forms its outputs o = tile.value(...) at their own positions and
 // writes them there (on a diagonal tile only the upper triangle).  The
 // mirrored half is written coalesced through an LDS transpose in PH phases
-// of 64 TM / PH tile rows (PH = 2 lets the waves of row group h stage their
-// rows in phase h), so `lds` needs (64 TM / PH) x (64 TN + 1) floats; it must
-// be free when this is called (the main loop has ended with a barrier).  The
-// accumulator layout is that of the 32 x 32 MFMA blocks, waves 2 x 2.
-template <int TM, int TN, int PH, class Tile>
+// of BM / PH tile rows; a wave's rows (32 TM of them, from wm) fall in one
+// phase, in which it stages them.  `lds` needs (BM / PH) x (BN + 1) floats
+// and must be free when this is called (the main loop has ended with a
+// barrier).  The accumulator layout is that of the 32 x 32 MFMA blocks; NT
+// threads take part.
+template <int TM, int TN, int BM, int BN, int NT, int PH, class Tile>
 __device__ __forceinline__ void sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN], float* lds, int m0, int n0,
                                              int wm, int wn, int lane, bool diag) {
-  constexpr int BN = 64 * TN, LD = BN + 1, RH = 64 * TM / PH;  // tile rows per phase
+  constexpr int LD = BN + 1, RH = BM / PH;  // tile rows per phase
+  static_assert(RH % (32 * TM) == 0, "a wave's rows must fall in one phase");
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int rl = wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
@@ -170,6 +172,10 @@ __device__ __forceinline__ void sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN]
         if (!diag || rl <= cl) tile.write(m0 + rl, n0 + cl, o);
         acc[i][j][e] = o;
       }
+      // with many accumulators, one 32 x 32 block at a time, so that the
+      // epilogue's own loads in flight need no registers beyond them
+      if constexpr (TM * TN > 4) __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
   for (int h = 0; h < PH; ++h) {
     if (PH == 1 || wm / RH == h) {
@@ -186,7 +192,7 @@ __device__ __forceinline__ void sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN]
     }
     __syncthreads();
     // o[h RH + b][a] goes to (n0 + a, m0 + h RH + b); on a diagonal tile only below the diagonal.
-    for (int idx = threadIdx.x; idx < RH * BN; idx += kGemmThreads) {
+    for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
       const int a = idx / RH, b = idx - (idx / RH) * RH;
       if (!diag || a > h * RH + b) tile.write(n0 + a, m0 + h * RH + b, lds[b * LD + a]);
     }
@@ -298,7 +304,8 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   typename Epi::Tile tile(P.e[job], item, P.B);
   if constexpr (Epi::kSym) {
     if (P.sym) {
-      sym_epilogue<TM, TN, kPipe >= BM * (BN + 1) ? 1 : 2>(tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
+      sym_epilogue<TM, TN, BM, BN, kGemmThreads, kPipe >= BM * (BN + 1) ? 1 : 2>(tile, acc, lds, m0, n0, wm, wn,
+                                                                                 lane, tm == tn);
       return;
     }
   }

@@ -706,7 +706,7 @@ int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int 
     SHP_TRY(run_ew<EW_CN16_START>(a, nf, st));
     SHP_TRY(run_resid(ws->partials, a.chunks, resid, iters, 0, status, nf, st));
   }
-  const int tiles = gemm_tiles(B);
+  const int tiles = (B / h16_tile_of(B, false)) * (B / h16_tile_of(B, false));  // partials of the full C^p M
   uint16_t* X = nullptr;
   for (int it = 0; it < iters; ++it) {
     if (it == iters - 1) {

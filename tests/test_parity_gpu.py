@@ -324,3 +324,53 @@ def test_coupled_newton_fp16_matches_oracle(B, p, iters, full):
     assert err <= TOL_BF16, err
     assert np.all(np.isfinite(Rh)) and np.all(Rh >= 0.0)
     report("cn_fp16", B=B, p=p, iters=iters, full=full, err=err)
+
+
+@pytest.mark.parametrize("B", [384, 512])
+def test_half_width_products_span_tiles(B):
+    """The 16-bit products on several tiles per factor: B = 384 runs the
+    128 x 128 workgroup tile (3 x 3 tiles), B = 512 the 256 x 256 one (2 x 2),
+    both with off-diagonal symmetric tiles and their mirrored writes:
+    bf16-input accumulation, Chebyshev (symmetric and full products), coupled
+    Newton on fp16 operands (with its tile reductions) and preconditioning."""
+    nf, n = 2, 2
+    G = grads(150 + B, n, B, 0.02)
+    F = torch.zeros((2 * n, B, B), dtype=torch.float32, device="cuda")
+    PL.accumulate(PL.BlockTable.from_stack(dev(G)), F, 0.0, 1.0, prec=capi.BF16_IN)
+    out = host(F)
+    err = 0.0
+    for i in range(n):
+        L, R = O.accumulate(np.zeros((B, B)), np.zeros((B, B)), G[i], 0.0, 1.0)
+        err = max(err, O.relative_frobenius(out[i], L), O.relative_frobenius(out[n + i], R))
+        assert np.array_equal(out[i], out[i].T) and np.array_equal(out[n + i], out[n + i].T)
+    assert err <= TOL_BF16, err
+    report("h16_tiles_accumulate", B=B, err=err)
+
+    Fs = W.spd_factors(151 + B, nf, B, cond=1e3)
+    V0 = W.start_vectors(152, nf, B)
+    Fd = dev(Fs)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    os_ = [oracle_scale(Fs[i], 0.0, capi.SCALE_POWER, V0[i]) for i in range(nf)]
+    for full in (False, True):
+        X, _ = gpu_roots(Fd, sc, st, "cheby", degree=8, prec=capi.BF16_IN | (capi.FULL_PRODUCTS if full else 0))
+        Xh = host(X)
+        err = max(O.relative_frobenius(Xh[i], oracle_root(Fs[i], os_[i], "cheby", degree=8)) for i in range(nf))
+        assert err <= TOL_BF16, err
+        if not full:
+            assert all(np.array_equal(Xh[i], Xh[i].T) for i in range(nf))
+        report("h16_tiles_cheby", B=B, full=full, err=err)
+    X, R = gpu_roots(Fd, sc, st, "newton", iters=4, p=4, variant=capi.CN_F16, resid=True)
+    Xh, Rh = host(X), host(R)
+    err = max(O.relative_frobenius(Xh[i], oracle_root(Fs[i], os_[i], "newton", iters=4, p=4, variant=capi.CN))
+              for i in range(nf))
+    assert err <= TOL_BF16, err
+    assert np.all(np.isfinite(Rh)) and np.all(Rh >= 0.0)
+    report("h16_tiles_cn_fp16", B=B, err=err)
+
+    Xp = np.concatenate([W.spd_factors(153 + B, n, B, cond=10.0), W.spd_factors(154 + B, n, B, cond=10.0)])
+    U = torch.full((n, B, B), float("nan"), dtype=torch.float32, device="cuda")
+    PL.precondition(dev(Xp), PL.BlockTable.from_stack(dev(G)), PL.BlockTable.from_stack(U), prec=capi.BF16_IN)
+    Uh = host(U)
+    err = max(O.relative_frobenius(Uh[i], O.precondition(Xp[i], G[i], Xp[n + i])) for i in range(n))
+    assert err <= TOL_BF16, err
+    report("h16_tiles_precondition", B=B, err=err)
