@@ -11,7 +11,9 @@ U = X_L G X_R.  The default workload is the 360M-shaped transformer step
 power-iteration scaling and Newton-DB (k = 10 per pass), all fp32.
 
 Prints one JSON line.  `value` is inverse-4th-root blocks (factors) per
-second of whole-step time.  `roofline` reports the dominant kernel (the
+second of whole-step time (with --workload c3-f10, where the roots are
+refreshed every 10th step, the roots computed per second over whole
+10-step periods; ms_per_step is then the amortised step).  `roofline` reports the dominant kernel (the
 Newton-DB pair product) from HIP events recorded around each of its launches
 during the timed steps; `cpu_baseline` times the float64 oracle on a bounded
 sample of the same workload on the host cores.
@@ -68,6 +70,11 @@ def workloads():
                         prec=capi.F32, nblocks=None,
                         name="360M-shaped optimizer step, B=1024, 576 factors, coupled Newton k=10 on fp16 "
                              "operands with fp32 accumulation (accumulate, scale, precondition fp32)"),
+        "c3-f10": dict(cfg=3, spec=W.MODEL_360M, B=1024, solver="newton", variant=capi.NDB_Z, iters=10,
+                       prec=capi.F32, nblocks=None, update_every=10, steps=10,
+                       name="360M-shaped optimizer steps, B=1024, 576 factors, Newton-DB k=10 (second pass "
+                            "Z-chained), fp32, roots refreshed every 10 steps and cached in between; timed over "
+                            "whole 10-step periods, value counts the roots computed"),
         "c5": dict(cfg=5, spec=W.MODEL_1_3B, B=2048, solver="cheby", variant=capi.NDB, degree=24, iters=0,
                    prec=capi.BF16_IN, nblocks=None,
                    name="1.3B-shaped optimizer step: 24 layers, hidden 2048, MLP 8192; B=2048, 288 blocks "
@@ -139,9 +146,10 @@ def cpu_baseline(wl, grads, budget_s):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 5; 10 for c3-f10)")
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="c3", choices=["c3", "c3-literal", "c3-share", "c3-cn", "c3-cn16", "c5"])
+    ap.add_argument("--workload", default="c3",
+                    choices=["c3", "c3-literal", "c3-share", "c3-cn", "c3-cn16", "c3-f10", "c5"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -163,12 +171,17 @@ def main(argv=None):
         return 1
     capi.load()
     wl = workloads()[args.workload]
+    if args.steps is None:
+        args.steps = wl.get("steps", 5)
+    every = wl.get("update_every", 1)
+    refreshes = -(-args.steps // every)  # root refreshes in the timed steps (the first one is a refresh)
     B = wl["B"]
     grads, tens, table, outs, utable = build_inputs(wl, torch, PL, W)
     n = table.n
     nf = 2 * n
     cfg = PL.StepConfig(B=B, beta=0.95, eps_rel=1e-12, solver=wl["solver"], variant=wl["variant"],
-                        iters=wl.get("iters", 10) or 10, degree=wl.get("degree", 24), prec=wl["prec"])
+                        iters=wl.get("iters", 10) or 10, degree=wl.get("degree", 24), prec=wl["prec"],
+                        update_every=every)
     state = PL.ShampooBlocks(cfg, n)
     state.set_start_vectors(torch.from_numpy(W.start_vectors(wl["cfg"], nf, B)).cuda())
     stream = torch.cuda.current_stream()
@@ -247,7 +260,7 @@ def main(argv=None):
         peak = PEAK_BF16_MFMA if bf else PEAK_F32_MFMA
         kname = ("gemm_bf16_nt_kernel<EpiClenshaw>" if bf else "gemm_f32_kernel<EpiClenshaw>") + \
             " (one symmetric Clenshaw product per factor, upper tiles)"
-    cap = max(1, per_step * args.steps)
+    cap = max(1, per_step * refreshes)
     kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]
     for e in kev:
         e.record(stream)  # materialise the underlying HIP events
@@ -255,6 +268,7 @@ def main(argv=None):
     handles = (ctypes.c_void_p * (2 * cap))(*[e.cuda_event for e in kev])
     capi.check(capi.shampoo_timing_hook(family, ctypes.addressof(handles), cap), "timing hook")
 
+    state.t = 0  # the timed steps start with a root refresh
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -268,7 +282,7 @@ def main(argv=None):
     status = state.status.cpu()
     elapsed = t1 - t0
     ms_step = 1e3 * elapsed / args.steps
-    value = nf * args.steps / elapsed
+    value = nf * refreshes / elapsed
     avg_ms = sum(durs) / len(durs) if durs else float("nan")
     achieved = flops_per_launch / (avg_ms * 1e-3) / 1e12
     traffic = None
@@ -292,7 +306,8 @@ def main(argv=None):
         "dtype": ("bf16-in/f32" if cfg.prec == capi.BF16_IN else
                   "f16-in/f32" if cfg.variant == capi.CN_F16 and cfg.solver == "newton" else "f32"),
         "data": "synthetic N(0, 0.02^2) gradients of the workload's weight shapes, seeded",
-        "config": {"workload": wl["name"], "B": B, "blocks": n, "factors": nf},
+        "config": dict({"workload": wl["name"], "B": B, "blocks": n, "factors": nf},
+                       **({"update_every": every} if every > 1 else {})),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": kname, "launches_timed": recorded, "avg_launch_ms": round(avg_ms, 4),

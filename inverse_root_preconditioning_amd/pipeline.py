@@ -193,11 +193,17 @@ class StepConfig:
     interval_eps: float = 1e-12
     prec: int = F32
     keep_resid: bool = False
+    update_every: int = 1       # roots refreshed at steps 1, 1 + f, 1 + 2f, ...; cached in between
 
 
 @dataclass
 class ShampooBlocks:
-    """State and workspaces for a fixed set of gradient blocks."""
+    """State and workspaces for a fixed set of gradient blocks.
+
+    The factors are accumulated at every step.  With update_every = f > 1 the
+    scale and the inverse roots are recomputed only at steps 1, 1 + f,
+    1 + 2f, ... (the pages' update frequency) and the cached roots
+    precondition the steps in between.  `t` counts the steps taken."""
     cfg: StepConfig
     nblocks: int
     device: object = "cuda"
@@ -215,16 +221,26 @@ class ShampooBlocks:
             self.resid = torch.zeros((2 * n, passes * self.cfg.iters), dtype=torch.float32, device=dev)
         self.ws = {k: Workspace(dev) for k in ("acc", "scale", "root", "pre")}
         self.v0 = None
+        if self.cfg.update_every < 1:
+            raise ValueError("update_every must be >= 1")
+        self.t = 0
 
     def set_start_vectors(self, v0):
         _check_f32_cuda(v0, "v0", (2 * self.nblocks, self.cfg.B, v0.shape[2]))
         self.v0 = v0
 
+    @property
+    def refresh_due(self):
+        """Whether the next step recomputes the roots."""
+        return self.t % self.cfg.update_every == 0
+
     def step(self, g_table, u_table, stream=None):
         c = self.cfg
         accumulate(g_table, self.factors, c.beta, 1.0 - c.beta, c.prec, self.ws["acc"], stream)
-        self.update_roots(stream)
+        if self.refresh_due:
+            self.update_roots(stream)
         precondition(self.roots, g_table, u_table, c.prec, self.ws["pre"], stream)
+        self.t += 1
 
     def update_roots(self, stream=None):
         c = self.cfg

@@ -560,3 +560,35 @@ def shampoo_step(L, R, G, alpha, gamma, eps_rel, mode, V0L, V0R, method,
     XL = invroot(Ln, scL, method, **kw)
     XR = invroot(Rn, scR, method, **kw)
     return dict(L=Ln, R=Rn, XL=XL, XR=XR, U=precondition(XL, G, XR), scL=scL, scR=scR)
+
+
+
+def shampoo_run(grads, alpha, gamma, eps_rel, mode, V0L, V0R, method, update_every=1,
+                steps=20, safety=2.0, iters=10, p=4, degree=24, delta=1e-12, chaining="Y"):
+    """Several optimizer steps on one block with the roots refreshed every
+    `update_every` steps and cached in between.
+
+    [DASH] "Scoreboard with context" quotes runs at update frequency f = 10,
+    where only every f-th step pays for the roots and the steps between are
+    cheap; "Required resources" keeps the inverse roots cached in memory.
+    Reading: the factors are accumulated at every step; the scale and the
+    roots are recomputed at steps 1, 1 + f, 1 + 2 f, ... (counting from 1)
+    from the factors of that step; every step preconditions its own gradient
+    with the most recent roots.  Starts from zero factors.
+
+    Returns a list of dicts (L, R, XL, XR, U, refreshed) per step.
+    """
+    n = grads[0].shape[0]
+    L = np.zeros((n, n))
+    R = np.zeros((n, n))
+    kw = dict(iters=iters, p=p, degree=degree, delta=delta, chaining=chaining)
+    out = []
+    XL = XR = None
+    for t, G in enumerate(grads):
+        L, R = accumulate(L, R, G, alpha, gamma)
+        refreshed = t % update_every == 0
+        if refreshed:
+            XL = invroot(L, scale_factor(L, eps_rel, mode, V0L, steps, safety), method, **kw)
+            XR = invroot(R, scale_factor(R, eps_rel, mode, V0R, steps, safety), method, **kw)
+        out.append(dict(L=L, R=R, XL=XL, XR=XR, U=precondition(XL, G, XR), refreshed=refreshed))
+    return out

@@ -249,3 +249,47 @@ def test_config5_sampled_bf16_chebyshev():
     picks, ef, ex, eu = sampled_parity(5, *run, B, "cheby", capi.NDB, 24, 10)
     report("config5", blocks=picks, factor_err=ef, root_err=ex, U_err=eu)
     assert ef <= TOL_BF16 and ex <= TOL_BF16 and eu <= TOL_BF16
+
+
+@pytest.mark.parametrize("f", [2, 5])
+def test_config2_update_frequency(f):
+    """Config 2's five steps with the roots refreshed every f steps (steps 1,
+    1 + f, ...) and cached in between, against the oracle's multi-step run on
+    sampled blocks; the cached roots are left untouched on the other steps."""
+    B, beta, eps_rel, k = 256, 0.95, 1e-12, 10
+    grads = [W.config2_gradient(t) for t in range(1, 6)]
+    cfg = PL.StepConfig(B=B, beta=beta, eps_rel=eps_rel, variant=capi.NDB_Z, iters=k, update_every=f)
+    gt = dev(grads[0])
+    table = PL.BlockTable.from_layers([gt], B)
+    n = table.n
+    state = PL.ShampooBlocks(cfg, n)
+    V0 = W.start_vectors(2, 2 * n, B)
+    state.set_start_vectors(dev(V0))
+    U = torch.empty_like(gt)
+    utable = PL.BlockTable.from_layers([U], B)
+    sample = (0, 6, n - 1)
+    runs = {}
+    for i in sample:
+        r0, c0 = (i // 4) * B, (i % 4) * B
+        runs[i] = O.shampoo_run([G[r0:r0 + B, c0:c0 + B] for G in grads], beta, 1 - beta, eps_rel, "power",
+                                V0[i], V0[n + i], "ndb", update_every=f, steps=20, safety=2.0, iters=k,
+                                chaining="Z")
+    prev = None
+    for t, G in enumerate(grads):
+        due = state.refresh_due
+        assert due == (t % f == 0)
+        gt.copy_(torch.from_numpy(G))
+        state.step(table, utable)
+        X, Uh = host(state.roots), host(U)
+        if not due:
+            assert np.array_equal(X, prev), "cached roots changed on a step without refresh"
+        prev = X
+        ex = eu = 0.0
+        for i in sample:
+            r0, c0 = (i // 4) * B, (i % 4) * B
+            o = runs[i][t]
+            assert o["refreshed"] == due
+            ex = max(ex, O.relative_frobenius(X[i], o["XL"]), O.relative_frobenius(X[n + i], o["XR"]))
+            eu = max(eu, O.relative_frobenius(Uh[r0:r0 + B, c0:c0 + B], o["U"]))
+        report("config2_update_frequency", f=f, step=t + 1, refreshed=due, root_err=ex, U_err=eu)
+        assert ex <= TOL_F32 and eu <= TOL_F32, (t, ex, eu)

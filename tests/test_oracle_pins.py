@@ -403,3 +403,32 @@ def test_graft_step_length_and_zero_update():
     same, _, _, s0 = O.graft_update(theta, np.zeros((8, 8)), np.zeros((8, 8)), g, np.zeros((8, 8)),
                                     0.1, 0.9, 0.999, 1e-8, 1)
     assert s0 == 0.0 and np.array_equal(same, theta)
+
+
+@pytest.mark.parametrize("f", [1, 2, 3])
+def test_update_frequency_schedule_and_cached_roots(f):
+    """Roots refreshed every f steps, cached in between, against closed forms:
+    the EMA factor after t steps is sum_s gamma alpha^(t-s) G_s G_s^T (and the
+    transpose form for R), and with eps = 0 the exact root does not depend on
+    the scale, so U_t = L_r^{-1/4} G_t R_r^{-1/4} with r the latest refresh
+    step (1, 1 + f, ...), the roots taken through LAPACK's eigh."""
+    gen = np.random.default_rng(19)
+    n, T, alpha, gamma = 8, 5, 0.9, 0.1
+    Gs = [gen.standard_normal((n, n)) for _ in range(T)]
+    V0 = gen.standard_normal((n, 4))
+    run = O.shampoo_run(Gs, alpha, gamma, 0.0, "power", V0, V0, "exact", update_every=f, steps=30)
+
+    def lapack_root(A):
+        w, Q = np.linalg.eigh(A)
+        return (Q * w ** -0.25) @ Q.T
+
+    for t in range(T):
+        L = sum(gamma * alpha ** (t - s) * Gs[s] @ Gs[s].T for s in range(t + 1))
+        R = sum(gamma * alpha ** (t - s) * Gs[s].T @ Gs[s] for s in range(t + 1))
+        assert O.relative_frobenius(run[t]["L"], L) <= 1e-14 and O.relative_frobenius(run[t]["R"], R) <= 1e-14
+        r = t - t % f
+        assert run[t]["refreshed"] == (r == t)
+        Lr = sum(gamma * alpha ** (r - s) * Gs[s] @ Gs[s].T for s in range(r + 1))
+        Rr = sum(gamma * alpha ** (r - s) * Gs[s].T @ Gs[s] for s in range(r + 1))
+        ref = lapack_root(Lr) @ Gs[t] @ lapack_root(Rr)
+        assert O.relative_frobenius(run[t]["U"], ref) <= 1e-10, (t, f)
