@@ -258,7 +258,7 @@ def main(argv=None):
         mfma_flops = nf * executed
         bf = cfg.prec == capi.BF16_IN
         peak = PEAK_BF16_MFMA if bf else PEAK_F32_MFMA
-        kname = ("gemm_bf16_nt_kernel<EpiClenshaw>" if bf else "gemm_f32_kernel<EpiClenshaw>") + \
+        kname = ("gemm_h16_nt_kernel<EpiClenshaw, bf16>" if bf else "gemm_f32_kernel<EpiClenshaw>") + \
             " (one symmetric Clenshaw product per factor, upper tiles)"
     cap = max(1, per_step * refreshes)
     kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]
