@@ -195,6 +195,11 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = (wave / WC) * 32 * TM, wn = (wave % WC) * 32 * TN;
   const int rr = lane & 31, h = lane >> 5;
+  // On a diagonal tile of a symmetric product a wave whose block lies wholly
+  // below the diagonal holds only entries that are never written: it skips
+  // its fragment reads and MFMAs but still stages operands and meets every
+  // barrier.
+  const bool active = CFG != H16_T128 || !(P.sym && tm == tn && wm >= wn + 32 * TN);
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -236,26 +241,32 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
   gload(0);
   sstore(lds);
   __syncthreads();
-  u32x4 ca[TM], cb[TN];
-  frags(lds, 0, ca, cb);
+  u32x4 ca[TM] = {}, cb[TN] = {};
+  if (active) frags(lds, 0, ca, cb);
   for (int s = 0; s < nstages; ++s) {
     const uint16_t* cur = lds + (s & 1) * kStage;
     if (s + 1 < nstages) gload((s + 1) * kBK16);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 na[TM], nb[TN];
+      u32x4 na[TM], nb[TN];  // the next k step's fragments (kept as they are when none are read)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) na[i] = ca[i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) nb[j] = cb[j];
       if (ks + 1 < KS) {
-        frags(cur, ks + 1, na, nb);
+        if (active) frags(cur, ks + 1, na, nb);
       } else if (s + 1 < nstages) {
         uint16_t* nxt = lds + ((s + 1) & 1) * kStage;
         sstore(nxt);
         __syncthreads();
-        frags(nxt, 0, na, nb);
+        if (active) frags(nxt, 0, na, nb);
       }
+      if (active) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma_h16<FMT>(ca[i], cb[j], acc[i][j]);
+          for (int j = 0; j < TN; ++j) acc[i][j] = mfma_h16<FMT>(ca[i], cb[j], acc[i][j]);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i) ca[i] = na[i];
 #pragma unroll

@@ -239,6 +239,11 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   const int wave = threadIdx.x >> 6;
   const int wm = (wave >> 1) * 32 * TM;  // wave's row offset inside the tile
   const int wn = (wave & 1) * 32 * TN;
+  // On a diagonal tile of a symmetric product the wave below the diagonal
+  // (rows 32 TM.., columns ..32 TN) holds only entries that are never
+  // written: it skips its fragment reads and MFMAs (it still stages operands
+  // and meets every barrier), which frees its SIMD for other workgroups.
+  const bool active = !(P.sym && tm == tn && wm > wn);
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -269,27 +274,29 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
     }
     // Fragments are double-buffered in registers: the reads for k-group g+1
     // are issued before the MFMAs of group g, so LDS latency hides behind them.
-    floatx4 fa[2][TM], fb[2][TN];
+    if (active) {
+      floatx4 fa[2][TM], fb[2][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = SA::frag(bufA, wm + 32 * i, 0, lane);
+      for (int i = 0; i < TM; ++i) fa[0][i] = SA::frag(bufA, wm + 32 * i, 0, lane);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = SB::frag(bufB, wn + 32 * j, 0, lane);
+      for (int j = 0; j < TN; ++j) fb[0][j] = SB::frag(bufB, wn + 32 * j, 0, lane);
 #pragma unroll
-    for (int g = 0; g < BK / 8; ++g) {
-      const int c = g & 1;
-      if (g + 1 < BK / 8) {
+      for (int g = 0; g < BK / 8; ++g) {
+        const int c = g & 1;
+        if (g + 1 < BK / 8) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[c ^ 1][i] = SA::frag(bufA, wm + 32 * i, g + 1, lane);
+          for (int i = 0; i < TM; ++i) fa[c ^ 1][i] = SA::frag(bufA, wm + 32 * i, g + 1, lane);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[c ^ 1][j] = SB::frag(bufB, wn + 32 * j, g + 1, lane);
+          for (int j = 0; j < TN; ++j) fb[c ^ 1][j] = SB::frag(bufB, wn + 32 * j, g + 1, lane);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
     }
     if (s + 1 < nstages) {
       float* nxt = lds + (cur ^ 1) * kStage;
