@@ -63,6 +63,11 @@ def workloads():
                          prec=capi.F32, nblocks=36,
                          name="one GPU's share of 8 of the 360M-shaped step: 36 blocks (72 factors) of "
                               "1024^2, Newton-DB k=10, fp32"),
+        "c3-symp": dict(cfg=3, spec=W.MODEL_360M, B=1024, solver="newton", variant=capi.NDB_Z | capi.SYM_COUPLING,
+                        iters=10, prec=capi.F32, nblocks=None,
+                        name="360M-shaped optimizer step, B=1024, 576 factors, Newton-DB k=10 (second pass "
+                             "Z-chained) with the opt-in symmetric coupling product P = Z Y (not the default: less "
+                             "stable on ill-conditioned factors), fp32"),
         "c3-cn": dict(cfg=3, spec=W.MODEL_360M, B=1024, solver="newton", variant=capi.CN, iters=10,
                       prec=capi.F32, nblocks=None,
                       name="360M-shaped optimizer step, B=1024, 576 factors, coupled Newton k=10, fp32"),
@@ -124,7 +129,7 @@ def cpu_baseline(wl, grads, budget_s):
     except Exception:
         pass
     method = "ndb" if wl["solver"] == "newton" else "cheby"
-    chaining = "Z" if wl["variant"] == capi.NDB_Z else "Y"
+    chaining = "Z" if (wl["variant"] & 0xff) == capi.NDB_Z else "Y"
     t0 = time.perf_counter()
     done = 0
     for i in range(n):
@@ -149,7 +154,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default 5; 10 for c3-f10)")
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="c3",
-                    choices=["c3", "c3-literal", "c3-share", "c3-cn", "c3-cn16", "c3-f10", "c5"])
+                    choices=["c3", "c3-literal", "c3-share", "c3-symp", "c3-cn", "c3-cn16", "c3-f10", "c5"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -238,11 +243,12 @@ def main(argv=None):
     sym_product = float(B) * B * (B + 1)
     tiles = B // 128 if B % 128 == 0 else B // 64
     executed = 2.0 * B ** 3 * (tiles * (tiles + 1) / 2) / tiles ** 2  # upper tiles incl. the diagonal ones
-    if cfg.solver == "newton" and cfg.variant in (capi.CN, capi.CN_F16):
+    base_variant = cfg.variant & 0xff  # without the modifier bits
+    if cfg.solver == "newton" and base_variant in (capi.CN, capi.CN_F16):
         family, per_step = capi.TIME_CN_M, cfg.iters - 1
         flops_per_launch = nf * 2.0 * B ** 3
         mfma_flops = flops_per_launch
-        half = cfg.variant == capi.CN_F16
+        half = base_variant == capi.CN_F16
         peak = PEAK_BF16_MFMA if half else PEAK_F32_MFMA
         kname = ("gemm_h16_nt_kernel<EpiCnM, fp16>" if half else "gemm_f32_kernel<EpiCnM>") + \
             " (coupled Newton C^p M, one full product per factor)"
@@ -304,7 +310,7 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("bf16-in/f32" if cfg.prec == capi.BF16_IN else
-                  "f16-in/f32" if cfg.variant == capi.CN_F16 and cfg.solver == "newton" else "f32"),
+                  "f16-in/f32" if (cfg.variant & 0xff) == capi.CN_F16 and cfg.solver == "newton" else "f32"),
         "data": "synthetic N(0, 0.02^2) gradients of the workload's weight shapes, seeded",
         "config": dict({"workload": wl["name"], "B": B, "blocks": n, "factors": nf},
                        **({"update_every": every} if every > 1 else {})),

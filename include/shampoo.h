@@ -91,9 +91,22 @@ enum {
  * polynomial in the factor -- Newton-DB's Y E and E Z, coupled Newton's X C
  * and powers of C, Clenshaw's A_s b -- is symmetric in exact arithmetic, so
  * only its upper-triangular tiles are computed and mirrored (the outputs are
- * exactly symmetric).  The coupling products Z Y and C^p M are always full.
- * With this bit set every product is computed in full. */
+ * exactly symmetric).  The coupling products Z Y and C^p M are computed in
+ * full by default.  With this bit set every product is computed in full. */
 #define SHAMPOO_FULL_PRODUCTS 0x100
+
+/* Opt-in modifier bit for shampoo_invroot_newton: form the coupling products
+ * (Newton-DB's P = Z Y, coupled Newton's C^p M) from upper tiles as well,
+ * which saves about 40% of their MFMA work.  They are symmetric in exact
+ * arithmetic, but with the full product the coupled iterations stay
+ * self-correcting: measured in fp32 on factors with a condition number of
+ * 1e8, the mirrored coupling product matches the full one while the
+ * iteration converges and then lets rounding errors grow until the iterates
+ * overflow (Newton-DB by k = 15 per pass, where the full product stays
+ * accurate); coupled Newton on fp16 operands loses accuracy the same way
+ * over many iterations.  Use only for well-conditioned factors or few
+ * iterations.  Ignored together with SHAMPOO_FULL_PRODUCTS. */
+#define SHAMPOO_SYM_COUPLING 0x200
 
 /* Operation ids of shampoo_workspace_bytes. */
 enum {

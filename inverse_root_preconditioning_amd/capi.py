@@ -38,6 +38,7 @@ CN = 2
 CN_F16 = 3
 # Modifier bit for variant (newton) / prec (cheby): compute symmetric products in full
 FULL_PRODUCTS = 0x100
+SYM_COUPLING = 0x200      # opt-in: coupling products from upper tiles (faster, less stable)
 # Workspace op ids
 OP_ACCUMULATE = 1
 OP_SCALE = 2

@@ -72,8 +72,9 @@ __device__ __forceinline__ floatx16 mfma_h16(const u32x4& a, const u32x4& b, con
 // epilogue's own loads are in flight.  For a symmetric product (`sym`) the
 // value formed at each computed position is written there (on a diagonal
 // tile only on and above the diagonal), kept in LDS, and written mirrored
-// through a transposed pass.  `lds` needs (BM / PH) x (BN + 1) floats and
-// must be free.  Returns this thread's share of the tile's reduction.
+// through a transposed pass, and the reduction is weighted as in
+// sym_epilogue.  `lds` needs (BM / PH) x (BN + 1) floats and must be free.
+// Returns this thread's share of the tile's reduction.
 template <int TM, int TN, int BM, int BN, int NT, int PH, class Epi>
 __device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, floatx16 (&acc)[TM][TN], float* lds,
                                                  int m0, int n0, int wm, int wn, int lane, bool sym, bool diag) {
@@ -100,6 +101,11 @@ __device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, float
       if (sym) {
         for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
           const int b = idx / BN, a = idx - (idx / BN) * BN;
+          if constexpr (Epi::kReduce) {  // weights as in sym_epilogue
+            const int rg = r0 + b, cg = n0 + a;
+            const float w = !diag ? 1.f : (rg < cg ? 2.f : (rg == cg ? 1.f : 0.f));
+            part += w * tile.contrib(rg, cg, lds[b * LD + a]);
+          }
           const float o = tile.value(r0 + b, n0 + a, lds[b * LD + a]);
           if (!diag || r0 + b <= n0 + a) tile.write(r0 + b, n0 + a, o);
           lds[b * LD + a] = o;
@@ -289,26 +295,30 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
       constexpr int PH = (sizeof(lds) >= sizeof(float) * BM * (BN + 1)) ? 1 : 2;
       static_assert(sizeof(lds) >= sizeof(float) * (BM / PH) * (BN + 1), "LDS too small for the transpose");
       if (P.sym) {
-        sym_epilogue<TM, TN, BM, BN, NT, PH>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, lane,
-                                             tm == tn);
-        return;
+        part = sym_epilogue<TM, TN, BM, BN, NT, PH, Epi::kReduce>(tile, acc, reinterpret_cast<float*>(lds), m0,
+                                                                   n0, wm, wn, lane, tm == tn);
       }
     }
+    if (!(Epi::kSym && P.sym)) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-          const int col = n0 + wn + 32 * j + rr;
-          part += tile.store(row, col, acc[i][j][e]);
-        }
+          for (int e = 0; e < 16; ++e) {
+            const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+            const int col = n0 + wn + 32 * j + rr;
+            part += tile.store(row, col, acc[i][j][e]);
+          }
+    }
   }
   if constexpr (Epi::kReduce) {
     __shared__ float red[NT / kWave];
     const float tot = block_sum<NT>(part, red);
-    if (threadIdx.x == 0) tile.partial(tm * P.tiles_n + tn, tot);
+    if (threadIdx.x == 0) {
+      tile.partial(tm * P.tiles_n + tn, tot);
+      if (P.sym && tm != tn) tile.partial(tn * P.tiles_n + tm, tot);  // the mirrored tile
+    }
   }
 }
 

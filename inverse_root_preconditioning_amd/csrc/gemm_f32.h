@@ -155,11 +155,17 @@ struct GemmLaunch {
 // and must be free when this is called (the main loop has ended with a
 // barrier).  The accumulator layout is that of the 32 x 32 MFMA blocks; NT
 // threads take part.
-template <int TM, int TN, int BM, int BN, int NT, int PH, class Tile>
-__device__ __forceinline__ void sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN], float* lds, int m0, int n0,
-                                             int wm, int wn, int lane, bool diag) {
+//
+// With RED, returns this thread's share of the tile's reduction of
+// tile.contrib(...) over the symmetric result: on a diagonal tile entries
+// above the diagonal count twice, diagonal entries once and entries below
+// not at all; an off-diagonal tile counts once and stands for its mirror too.
+template <int TM, int TN, int BM, int BN, int NT, int PH, bool RED = false, class Tile>
+__device__ __forceinline__ float sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN], float* lds, int m0, int n0,
+                                              int wm, int wn, int lane, bool diag) {
   constexpr int LD = BN + 1, RH = BM / PH;  // tile rows per phase
   static_assert(RH % (32 * TM) == 0, "a wave's rows must fall in one phase");
+  float part = 0.f;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -168,13 +174,17 @@ __device__ __forceinline__ void sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN]
       for (int e = 0; e < 16; ++e) {
         const int rl = wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         const int cl = wn + 32 * j + (lane & 31);
+        if constexpr (RED) {
+          const float w = !diag ? 1.f : (rl < cl ? 2.f : (rl == cl ? 1.f : 0.f));
+          part += w * tile.contrib(m0 + rl, n0 + cl, acc[i][j][e]);
+        }
         const float o = tile.value(m0 + rl, n0 + cl, acc[i][j][e]);
         if (!diag || rl <= cl) tile.write(m0 + rl, n0 + cl, o);
         acc[i][j][e] = o;
       }
-      // with many accumulators, one 32 x 32 block at a time, so that the
-      // epilogue's own loads in flight need no registers beyond them
-      if constexpr (TM * TN > 4) __builtin_amdgcn_sched_barrier(0);
+      // one 32 x 32 block at a time, so that the epilogue's own loads in
+      // flight need few registers beyond the accumulators
+      if constexpr (TM * TN > 4 || RED) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
   for (int h = 0; h < PH; ++h) {
@@ -198,6 +208,7 @@ __device__ __forceinline__ void sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN]
     }
     if (h + 1 < PH) __syncthreads();
   }
+  return part;
 }
 
 template <int TM, int TN, int LA, int LB, bool DA, bool DB, class Epi, int BK = kBK, int MINW = 2>
@@ -309,27 +320,33 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   // Epilogue.  Accumulator e of block (i, j) sits at
   // row = 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = 32 j + lane % 32.
   typename Epi::Tile tile(P.e[job], item, P.B);
+  float part = 0.f;
+  bool done = false;
   if constexpr (Epi::kSym) {
     if (P.sym) {
-      sym_epilogue<TM, TN, BM, BN, kGemmThreads, kPipe >= BM * (BN + 1) ? 1 : 2>(tile, acc, lds, m0, n0, wm, wn,
-                                                                                 lane, tm == tn);
-      return;
+      part = sym_epilogue<TM, TN, BM, BN, kGemmThreads, kPipe >= BM * (BN + 1) ? 1 : 2, Epi::kReduce>(
+          tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
+      done = true;
     }
   }
-  float part = 0.f;
+  if (!done) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int col = n0 + wn + 32 * j + (lane & 31);
-        part += tile.store(row, col, acc[i][j][e]);
-      }
-  if (Epi::kReduce) {
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int col = n0 + wn + 32 * j + (lane & 31);
+          part += tile.store(row, col, acc[i][j][e]);
+        }
+  }
+  if constexpr (Epi::kReduce) {
     const float tot = block_sum<kGemmThreads>(part, red);
-    if (threadIdx.x == 0) tile.partial(tm * P.tiles_n + tn, tot);
+    if (threadIdx.x == 0) {
+      tile.partial(tm * P.tiles_n + tn, tot);
+      if (P.sym && tm != tn) tile.partial(tn * P.tiles_n + tm, tot);  // the mirrored tile
+    }
   }
 }
 
@@ -429,9 +446,11 @@ struct EpiStoreDesc {
   };
 };
 
-// Newton-DB: P = Z Y -> E = (3 I - P) / 2, reduction ||I - P||_F^2.
+// Newton-DB: P = Z Y -> E = (3 I - P) / 2, reduction ||I - P||_F^2.  Z and
+// Y are polynomials in A_s, so P is symmetric and may be formed from upper
+// tiles.
 struct EpiNdbE {
-  static constexpr bool kSym = false;
+  static constexpr bool kSym = true;
   static constexpr bool kReduce = true;
   struct Job {
     float* e;
@@ -446,20 +465,27 @@ struct EpiNdbE {
       e = j.e + item * (int64_t)B_ * B_;
       part = j.partials + item * j.tiles;
     }
-    __device__ __forceinline__ float store(int row, int col, float v) {
-      const float d = (row == col) ? 1.f : 0.f;
-      stg(e + (int64_t)row * B + col, 1.5f * d - 0.5f * v);
-      const float r = d - v;
+    __device__ __forceinline__ float value(int row, int col, float v) const {
+      return 1.5f * ((row == col) ? 1.f : 0.f) - 0.5f * v;
+    }
+    __device__ __forceinline__ void write(int row, int col, float o) { stg(e + (int64_t)row * B + col, o); }
+    __device__ __forceinline__ float contrib(int row, int col, float v) const {
+      const float r = ((row == col) ? 1.f : 0.f) - v;
       return r * r;
+    }
+    __device__ __forceinline__ float store(int row, int col, float v) {
+      write(row, col, value(row, col, v));
+      return contrib(row, col, v);
     }
     __device__ void partial(int t, float s) { stg(part + t, s); }
   };
 };
 
 // Coupled Newton: M' = C^p M -> store M' and C' = ((p+1) I - M') / p,
-// reduction ||I - M'||_F^2.
+// reduction ||I - M'||_F^2.  C^p and M are polynomials in A_s, so M' is
+// symmetric and may be formed from upper tiles.
 struct EpiCnM {
-  static constexpr bool kSym = false;
+  static constexpr bool kSym = true;
   static constexpr bool kReduce = true;
   struct Job {
     float* m;            // fp32 outputs (null: not written)
@@ -491,16 +517,23 @@ struct EpiCnM {
       p1 = j.p + 1.f;
       pinv = 1.f / j.p;
     }
-    __device__ __forceinline__ float store(int row, int col, float v) {
+    __device__ __forceinline__ float value(int, int, float v) const { return v; }
+    // M' = o at (row, col) and the matching entry of C'
+    __device__ __forceinline__ void write(int row, int col, float o) {
       const int64_t idx = (int64_t)row * B + col;
-      const float d = (row == col) ? 1.f : 0.f;
-      const float cv = (p1 * d - v) * pinv;
-      if (m) stg(m + idx, v);
+      const float cv = (p1 * ((row == col) ? 1.f : 0.f) - o) * pinv;
+      if (m) stg(m + idx, o);
       if (c) stg(c + idx, cv);
-      if (m16) stg(m16 + idx, to_h16(v, fmt));
+      if (m16) stg(m16 + idx, to_h16(o, fmt));
       if (c16) stg(c16 + idx, to_h16(cv, fmt));
-      const float r = d - v;
+    }
+    __device__ __forceinline__ float contrib(int row, int col, float v) const {
+      const float r = ((row == col) ? 1.f : 0.f) - v;
       return r * r;
+    }
+    __device__ __forceinline__ float store(int row, int col, float v) {
+      write(row, col, v);
+      return contrib(row, col, v);
     }
     __device__ void partial(int t, float s) { stg(part + t, s); }
   };

@@ -371,7 +371,8 @@ struct NdbCtx {
   int32_t* status;
   NewtonWs* ws;
   hipStream_t st;
-  bool sym;  // the updates Y E and E Z are symmetric: upper tiles only
+  bool sym;    // the updates Y E and E Z are symmetric: upper tiles only
+  bool sym_p;  // P = Z Y from upper tiles too (opt-in, see SHAMPOO_SYM_COUPLING)
 };
 
 // One Newton-DB pass.  The prologue reads `src` and forms Y0 = a src + b I
@@ -474,7 +475,7 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
       j.tiles = tiles;
       const float* A[1] = {Z};
       const float* Bm[1] = {Y};
-      SHP_TRY(gemm_nn<EpiNdbE>(A, Bm, &j, 1, nf, B, c.st, false, SHAMPOO_TIME_NDB_P));
+      SHP_TRY(gemm_nn<EpiNdbE>(A, Bm, &j, 1, nf, B, c.st, c.sym_p, SHAMPOO_TIME_NDB_P));
       SHP_TRY(run_resid(c.ws->partials, tiles, c.resid, c.ncols, pass * c.iters + it, c.status, nf, c.st));
     }
     const bool last = (it == c.iters - 1);
@@ -509,8 +510,8 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
 }
 
 int newton_db(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, bool zchain, int iters,
-              float* x, float* resid, int32_t* status, NewtonWs* ws, hipStream_t st, bool sym) {
-  NdbCtx c{nf, B, iters, resid, (p == 2 ? 1 : 2) * iters, status, ws, st, sym};
+              float* x, float* resid, int32_t* status, NewtonWs* ws, hipStream_t st, bool sym, bool sym_c) {
+  NdbCtx c{nf, B, iters, resid, (p == 2 ? 1 : 2) * iters, status, ws, st, sym, sym_c};
   FinalOut fo{x, sc, status, -1.f / (float)p, 1.f};
   float* r1 = nullptr;
   if (p == 2) return ndb_pass(c, F, false, sc, 0.f, 0.f, false, 0, fo, &r1);
@@ -531,7 +532,7 @@ int newton_db(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
 // Coupled Newton.
 // ---------------------------------------------------------------------------
 int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, int iters, float* x,
-                   float* resid, int32_t* status, NewtonWs* ws, hipStream_t st, bool sym) {
+                   float* resid, int32_t* status, NewtonWs* ws, hipStream_t st, bool sym, bool sym_c) {
   Pool& pool = ws->pool;
   float* M = pool.get();
   if (M == nullptr) return SHAMPOO_EWORKSPACE;
@@ -634,7 +635,7 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
       j.p = (float)p;
       const float* A[1] = {Cp};
       const float* Bm[1] = {M};
-      SHP_TRY(gemm_nn<EpiCnM>(A, Bm, &j, 1, nf, B, st, false, SHAMPOO_TIME_CN_M));
+      SHP_TRY(gemm_nn<EpiCnM>(A, Bm, &j, 1, nf, B, st, sym_c, SHAMPOO_TIME_CN_M));
       SHP_TRY(run_resid(ws->partials, tiles, resid, iters, it + 1, status, nf, st));
     }
     if (Cp != C) pool.put(Cp);
@@ -658,7 +659,7 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
 // exact arithmetic, and their rounding asymmetry is far below fp16 precision.
 // ---------------------------------------------------------------------------
 int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, int iters, float* x,
-                       float* resid, int32_t* status, Cn16Ws* ws, hipStream_t st, bool sym) {
+                       float* resid, int32_t* status, Cn16Ws* ws, hipStream_t st, bool sym, bool sym_c) {
   const float pexp = -1.f / (float)p;
   if (iters == 1) {  // X_1 = C_0: no product
     EwArgs a;
@@ -706,7 +707,7 @@ int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int 
     SHP_TRY(run_ew<EW_CN16_START>(a, nf, st));
     SHP_TRY(run_resid(ws->partials, a.chunks, resid, iters, 0, status, nf, st));
   }
-  const int tiles = (B / h16_tile_of(B, false)) * (B / h16_tile_of(B, false));  // partials of the full C^p M
+  const int tiles = (B / h16_tile_of(B, sym_c)) * (B / h16_tile_of(B, sym_c));  // reduction partials of C^p M
   uint16_t* X = nullptr;
   for (int it = 0; it < iters; ++it) {
     if (it == iters - 1) {
@@ -770,7 +771,7 @@ int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int 
       const uint16_t* A[1] = {Cp};
       const uint16_t* Bt[1] = {M};
       timing_before(SHAMPOO_TIME_CN_M, st);
-      const int rc = h16_gemm_nt<EpiCnM>(A, Bt, &j, 1, nf, B, false, H16_F16, st);
+      const int rc = h16_gemm_nt<EpiCnM>(A, Bt, &j, 1, nf, B, sym_c, H16_F16, st);
       timing_after(SHAMPOO_TIME_CN_M, st);
       SHP_TRY(rc);
       SHP_TRY(run_resid(ws->partials, tiles, resid, iters, it + 1, status, nf, st));
@@ -907,7 +908,7 @@ const char* shampoo_strerror(int code) {
 
 size_t shampoo_workspace_bytes(int op, int64_t count, int B, int variant_or_degree, int prec) {
   prec &= ~SHAMPOO_FULL_PRODUCTS;
-  if (op == SHAMPOO_OP_NEWTON) variant_or_degree &= ~SHAMPOO_FULL_PRODUCTS;
+  if (op == SHAMPOO_OP_NEWTON) variant_or_degree &= ~(SHAMPOO_FULL_PRODUCTS | SHAMPOO_SYM_COUPLING);
   if (count < 0 || !valid_B(B)) return 0;
   if (prec != SHAMPOO_F32 && prec != SHAMPOO_BF16_IN) return 0;
   Carver c(nullptr);
@@ -1031,7 +1032,8 @@ int shampoo_invroot_newton(const float* factors, const shampoo_scale* scale, int
                            int variant, int iters, float* x_out, float* resid_out, int32_t* status, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
   const bool sym = (variant & SHAMPOO_FULL_PRODUCTS) == 0;
-  variant &= ~SHAMPOO_FULL_PRODUCTS;
+  const bool sym_c = sym && (variant & SHAMPOO_SYM_COUPLING) != 0;
+  variant &= ~(SHAMPOO_FULL_PRODUCTS | SHAMPOO_SYM_COUPLING);
   if (nfactors < 0) return SHAMPOO_EINVAL;
   if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
   if (variant < SHAMPOO_NDB || variant > SHAMPOO_CN_F16) return SHAMPOO_EINVAL;
@@ -1051,14 +1053,15 @@ int shampoo_invroot_newton(const float* factors, const shampoo_scale* scale, int
   if (variant == SHAMPOO_CN_F16) {
     Cn16Ws w16;
     cn16_layout(c, nfactors, B, &w16);
-    return coupled_newton_h16(factors, scale, nfactors, B, p, iters, x_out, resid_out, status, &w16, stream, sym);
+    return coupled_newton_h16(factors, scale, nfactors, B, p, iters, x_out, resid_out, status, &w16, stream, sym,
+                              sym_c);
   }
   NewtonWs w;
   newton_layout(c, nfactors, B, variant, &w);
   if (variant == SHAMPOO_CN)
-    return coupled_newton(factors, scale, nfactors, B, p, iters, x_out, resid_out, status, &w, stream, sym);
+    return coupled_newton(factors, scale, nfactors, B, p, iters, x_out, resid_out, status, &w, stream, sym, sym_c);
   return newton_db(factors, scale, nfactors, B, p, variant == SHAMPOO_NDB_Z, iters, x_out, resid_out, status, &w,
-                   stream, sym);
+                   stream, sym, sym_c);
 }
 
 int shampoo_invroot_cheby(const float* factors, const shampoo_scale* scale, int64_t nfactors, int B, int p,

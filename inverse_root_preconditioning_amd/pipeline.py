@@ -217,7 +217,7 @@ class ShampooBlocks:
         self.scale, self.status = new_scale(2 * n, dev)
         self.resid = None
         if self.cfg.keep_resid and self.cfg.solver == "newton":
-            passes = 1 if (self.cfg.p == 2 or self.cfg.variant in (capi.CN, capi.CN_F16)) else 2
+            passes = 1 if (self.cfg.p == 2 or (self.cfg.variant & 0xff) in (capi.CN, capi.CN_F16)) else 2
             self.resid = torch.zeros((2 * n, passes * self.cfg.iters), dtype=torch.float32, device=dev)
         self.ws = {k: Workspace(dev) for k in ("acc", "scale", "root", "pre")}
         self.v0 = None

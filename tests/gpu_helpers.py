@@ -53,7 +53,7 @@ def gpu_roots(F, sc, st, method, iters=10, p=4, variant=capi.NDB, degree=24, del
     R = None
     if method == "newton":
         if resid:
-            passes = 1 if (p == 2 or (variant & ~capi.FULL_PRODUCTS) in (capi.CN, capi.CN_F16)) else 2
+            passes = 1 if (p == 2 or (variant & 0xff) in (capi.CN, capi.CN_F16)) else 2
             R = torch.full((F.shape[0], passes * iters), -1.0, dtype=torch.float32, device=F.device)
         PL.invroot_newton(F, sc, p, variant, iters, X, st, R)
     else:

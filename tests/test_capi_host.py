@@ -71,6 +71,11 @@ def test_workspace_sizes():
     assert ws(capi.OP_NEWTON, -1, B, capi.NDB, capi.F32) == 0
     assert ws(99, nf, B, 0, capi.F32) == 0
     assert ws(capi.OP_NEWTON, nf, B, 7, capi.F32) == 0
+    # modifier bits do not change the workspace
+    for v in (capi.NDB, capi.NDB_Z, capi.CN, capi.CN_F16):
+        base = ws(capi.OP_NEWTON, nf, B, v, capi.F32)
+        assert ws(capi.OP_NEWTON, nf, B, v | capi.SYM_COUPLING, capi.F32) == base
+        assert ws(capi.OP_NEWTON, nf, B, v | capi.FULL_PRODUCTS, capi.F32) == base
 
 
 def test_validation_codes_without_gpu():
@@ -86,6 +91,10 @@ def test_validation_codes_without_gpu():
     assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 64, 4, 9, 5, FAKE, 0, FAKE, FAKE, 1 << 40, 0) == f.EINVAL
     assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 192, 4, f.CN_F16, 5, FAKE, 0, FAKE, FAKE, 1 << 40, 0) == f.EUNSUPPORTED
     assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 256, 3, f.CN_F16, 5, FAKE, 0, FAKE, FAKE, 1 << 40, 0) == f.EUNSUPPORTED
+    assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 100, 4, f.NDB_Z | f.SYM_COUPLING, 5, FAKE, 0, FAKE, FAKE, 1 << 40,
+                                    0) == f.EUNSUPPORTED
+    assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 64, 4, 9 | f.SYM_COUPLING, 5, FAKE, 0, FAKE, FAKE, 1 << 40,
+                                    0) == f.EINVAL
     # null pointers and workspace
     assert f.shampoo_invroot_newton(0, FAKE, 4, 64, 4, f.NDB, 5, FAKE, 0, FAKE, FAKE, 1 << 40, 0) == f.EINVAL
     assert f.shampoo_invroot_newton(FAKE, FAKE, 4, 64, 4, f.NDB, 5, FAKE, 0, FAKE, FAKE, 16, 0) == f.EWORKSPACE

@@ -233,6 +233,17 @@ def test_config3_sampled(variant):
 
 
 @pytest.mark.slow
+def test_config3_sampled_symmetric_coupling():
+    """The opt-in symmetric coupling product (P = Z Y from upper tiles) on the
+    360M-shaped step with Newton-DB k = 10, Z-chained, as the benchmark runs it."""
+    B = 1024
+    run = model_step(3, W.MODEL_360M, B, "newton", variant=capi.NDB_Z | capi.SYM_COUPLING)
+    picks, ef, ex, eu = sampled_parity(3, *run, B, "newton", capi.NDB_Z, 24, 10)
+    report("config3_sym_coupling", blocks=picks, factor_err=ef, root_err=ex, U_err=eu)
+    assert ef <= 1e-5 and ex <= TOL_F32 and eu <= TOL_F32
+
+
+@pytest.mark.slow
 def test_config3_sampled_coupled_newton_fp16():
     """The pages' fastest configuration (coupled Newton in FP16) on the 360M-shaped step."""
     B = 1024

@@ -374,3 +374,30 @@ def test_half_width_products_span_tiles(B):
     err = max(O.relative_frobenius(Uh[i], O.precondition(Xp[i], G[i], Xp[n + i])) for i in range(n))
     assert err <= TOL_BF16, err
     report("h16_tiles_precondition", B=B, err=err)
+
+
+@pytest.mark.parametrize("variant,iters,tol", [(capi.NDB_Z, 6, TOL_F32), (capi.NDB, 6, TOL_F32), (capi.CN, 8, TOL_F32),
+                                              (capi.CN_F16, 8, TOL_BF16)])
+def test_symmetric_coupling_opt_in(variant, iters, tol):
+    """SHAMPOO_SYM_COUPLING forms Z Y (and C^p M) from upper tiles: on moderately
+    conditioned factors and a few iterations it matches the oracle like the
+    default, its residuals agree with the default's, and the roots are exactly
+    symmetric."""
+    nf, B = 4, 256
+    F = W.spd_factors(160, nf, B, cond=1e3)
+    V0 = W.start_vectors(161, nf, B)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    X, R = gpu_roots(Fd, sc, st, "newton", iters=iters, p=4, variant=variant | capi.SYM_COUPLING, resid=True)
+    _, R0 = gpu_roots(Fd, sc, st, "newton", iters=iters, p=4, variant=variant, resid=True)
+    Xh, Rh, R0h = host(X), host(R), host(R0)
+    base = capi.CN if variant == capi.CN_F16 else variant
+    err = 0.0
+    for i in range(nf):
+        o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
+        err = max(err, O.relative_frobenius(Xh[i], oracle_root(F[i], o, "newton", iters=iters, p=4, variant=base)))
+        assert np.array_equal(Xh[i], Xh[i].T)
+    assert err <= tol, err
+    # the weighted tile reductions give the same residual norms as the full products
+    assert np.allclose(Rh, R0h, rtol=2e-2 if variant == capi.CN_F16 else 1e-3, atol=1e-4), (Rh, R0h)
+    report("sym_coupling", variant=variant, iters=iters, err=err)
