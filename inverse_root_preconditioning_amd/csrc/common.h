@@ -87,6 +87,14 @@ __device__ __forceinline__ uint16_t to_h16(float x, int fmt) {
   return fmt == H16_F16 ? f32_to_f16_bits(x) : f32_to_bf16_bits(x);
 }
 
+// Four consecutive 16-bit copies of o at p (p 8-byte aligned).
+__device__ __forceinline__ void stg4_h16(uint16_t* p, const floatx4& o, int fmt) {
+  u32x2 w;
+  w.x = (uint32_t)to_h16(o[0], fmt) | ((uint32_t)to_h16(o[1], fmt) << 16);
+  w.y = (uint32_t)to_h16(o[2], fmt) | ((uint32_t)to_h16(o[3], fmt) << 16);
+  stg(reinterpret_cast<u32x2*>(p), w);
+}
+
 __device__ __forceinline__ bool degenerate(int32_t st) {
   return (st & (SHAMPOO_BLK_ZERO | SHAMPOO_BLK_NONPOS_RQ)) != 0;
 }

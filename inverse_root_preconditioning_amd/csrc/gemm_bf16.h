@@ -26,7 +26,7 @@ struct EpiStoreBf16 {
   struct Tile {
     uint16_t* out;
     int B;
-    __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) { out = j.out + item * (int64_t)B_ * B_; }
+    __device__ __forceinline__ Tile(const Job& j, int64_t item, int B_) : B(B_) { out = j.out + item * (int64_t)B_ * B_; }
     __device__ __forceinline__ float store(int row, int col, float v) {
       stg(out + (int64_t)row * B + col, f32_to_bf16_bits(v));
       return 0.f;
@@ -127,6 +127,41 @@ __device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, float
     if (h + 1 < PH) __syncthreads();
   }
   return part;
+}
+
+// Epilogue of a symmetric product without LDS (kDirect epilogues).  For each
+// group of four accumulators a lane holds rows r..r+3 of one column c: it
+// writes them there (on a diagonal tile only on and above the diagonal) and
+// writes the mirrored entries, columns r..r+3 of row c, with one vector
+// store (on a diagonal tile only those strictly below the diagonal).
+template <int TM, int TN, class Tile>
+__device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[TM][TN], int m0, int n0, int wm,
+                                                    int wn, int lane, bool diag) {
+  const int h = lane >> 5, cl = lane & 31;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
+        const int c = n0 + wn + 32 * j + cl;
+        floatx4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
+        const floatx4 o = tile.value4(r, c, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!diag || r + e <= c) tile.write(r + e, c, o[e]);
+        if (!diag || r + 3 < c) {
+          tile.write4t(c, r, o);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (r + e < c) tile.write(c, r + e, o[e]);
+        }
+      }
+    }
 }
 
 // Workgroup shapes of the 16-bit product.  The LDS traffic per MFMA falls
@@ -281,9 +316,7 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
   }
   __syncthreads();  // the LDS is reused by the epilogue
 
-  typename Epi::Job job_args = P.e[0];
-  if (job != 0) job_args = P.e[1];
-  typename Epi::Tile tile(job_args, item, P.B);
+  typename Epi::Tile tile(*(job == 0 ? &P.e[0] : &P.e[1]), item, P.B);
   float part = 0.f;
   if constexpr (CFG == H16_T256) {
     constexpr int PH = (sizeof(lds) >= sizeof(float) * BM * (BN + 1)) ? 1 : 2;
@@ -295,8 +328,11 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
       constexpr int PH = (sizeof(lds) >= sizeof(float) * BM * (BN + 1)) ? 1 : 2;
       static_assert(sizeof(lds) >= sizeof(float) * (BM / PH) * (BN + 1), "LDS too small for the transpose");
       if (P.sym) {
-        part = sym_epilogue<TM, TN, BM, BN, NT, PH, Epi::kReduce>(tile, acc, reinterpret_cast<float*>(lds), m0,
-                                                                   n0, wm, wn, lane, tm == tn);
+        if constexpr (Epi::kDirect && !Epi::kReduce)
+          sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn);
+        else
+          part = sym_epilogue<TM, TN, BM, BN, NT, PH, Epi::kReduce>(tile, acc, reinterpret_cast<float*>(lds), m0,
+                                                                     n0, wm, wn, lane, tm == tn);
       }
     }
     if (!(Epi::kSym && P.sym)) {

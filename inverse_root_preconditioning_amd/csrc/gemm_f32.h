@@ -358,6 +358,9 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
 // write(row, col, o) for symmetric products; there the output at a mirrored
 // position is the value formed at the computed one, which assumes the other
 // inputs of the epilogue (an EMA state, Clenshaw terms) are symmetric too.
+// Those with kDirect also provide value4(r, c, v) for rows r..r+3 of column c
+// and write4t(c, r, o), which writes o to row c, columns r..r+3 (the
+// mirrored entries) with vector stores.
 // ---------------------------------------------------------------------------
 
 // out = mult * acc + beta * cin (cin may alias out); X = I for a degenerate
@@ -366,6 +369,7 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
 struct EpiStore {
   static constexpr bool kReduce = false;
   static constexpr bool kSym = true;
+  static constexpr bool kDirect = true;
   struct Job {
     float* out;          // fp32 output (may be null when only the 16-bit copy is needed)
     const float* cin;
@@ -384,7 +388,7 @@ struct EpiStore {
     float mult, beta;
     bool ident;
     int B;
-    __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
+    __device__ __forceinline__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
       const int64_t off = item * (int64_t)B_ * B_;
       out = j.out ? j.out + off : nullptr;
       cin = j.cin ? j.cin + off : nullptr;
@@ -405,6 +409,17 @@ struct EpiStore {
       const int64_t idx = (int64_t)row * B + col;
       if (out) stg(out + idx, o);
       if (o16) stg(o16 + idx, to_h16(o, fmt));
+    }
+    __device__ __forceinline__ floatx4 value4(int r, int c, const floatx4& v) const {
+      floatx4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = value(r + e, c, v[e]);
+      return o;
+    }
+    __device__ __forceinline__ void write4t(int c, int r, const floatx4& o) {
+      const int64_t idx = (int64_t)c * B + r;
+      if (out) stg(reinterpret_cast<floatx4*>(out + idx), o);
+      if (o16) stg4_h16(o16 + idx, o, fmt);
     }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));
@@ -429,7 +444,7 @@ struct EpiStoreDesc {
     float* p;
     int64_t ld;
     int rows, cols;
-    __device__ Tile(const Job& j, int64_t item, int B) {
+    __device__ __forceinline__ Tile(const Job& j, int64_t item, int B) {
       const shampoo_block d = j.out[item];
       const bool ok = d.ptr != nullptr && d.rows >= 0 && d.cols >= 0 && d.rows <= B && d.cols <= B &&
                       d.ld >= d.cols;
@@ -451,6 +466,7 @@ struct EpiStoreDesc {
 // tiles.
 struct EpiNdbE {
   static constexpr bool kSym = true;
+  static constexpr bool kDirect = false;
   static constexpr bool kReduce = true;
   struct Job {
     float* e;
@@ -461,7 +477,7 @@ struct EpiNdbE {
     float* e;
     float* part;
     int B;
-    __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
+    __device__ __forceinline__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
       e = j.e + item * (int64_t)B_ * B_;
       part = j.partials + item * j.tiles;
     }
@@ -486,6 +502,7 @@ struct EpiNdbE {
 // symmetric and may be formed from upper tiles.
 struct EpiCnM {
   static constexpr bool kSym = true;
+  static constexpr bool kDirect = false;
   static constexpr bool kReduce = true;
   struct Job {
     float* m;            // fp32 outputs (null: not written)
@@ -506,7 +523,7 @@ struct EpiCnM {
     float* part;
     float p1, pinv;
     int B;
-    __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
+    __device__ __forceinline__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
       const int64_t off = item * (int64_t)B_ * B_;
       m = j.m ? j.m + off : nullptr;
       c = j.c ? j.c + off : nullptr;
@@ -546,6 +563,7 @@ struct EpiCnM {
 struct EpiClenshaw {
   static constexpr bool kReduce = false;
   static constexpr bool kSym = true;
+  static constexpr bool kDirect = true;
   struct Job {
     float* out;
     uint16_t* out16;     // optional 16-bit copy of b (operand of the next product)
@@ -567,7 +585,7 @@ struct EpiClenshaw {
     float cj, mult, k1, k2;
     bool ident;
     int B;
-    __device__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
+    __device__ __forceinline__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
       const int64_t off = item * (int64_t)B_ * B_;
       out = j.out + off;
       obf = j.out16 ? j.out16 + off : nullptr;
@@ -598,6 +616,25 @@ struct EpiClenshaw {
       const int64_t idx = (int64_t)row * B + col;
       stg(out + idx, o);
       if (obf) stg(obf + idx, to_h16(o, fmt));
+    }
+    // b1 and b2 come from symmetric steps (mirrored writes), so they are read
+    // at the transposed position: row c, columns r..r+3, one vector load each.
+    __device__ __forceinline__ floatx4 value4(int r, int c, const floatx4& v) const {
+      const int64_t idx = (int64_t)c * B + r;
+      const floatx4 x1 = ldg(reinterpret_cast<const floatx4*>(b1 + idx));
+      const floatx4 x2 = ldg(reinterpret_cast<const floatx4*>(b2 + idx));
+      floatx4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool dg = (r + e == c);
+        o[e] = ident ? (dg ? 1.f : 0.f) : mult * ((dg ? cj : 0.f) + k1 * v[e] - k2 * x1[e] - x2[e]);
+      }
+      return o;
+    }
+    __device__ __forceinline__ void write4t(int c, int r, const floatx4& o) {
+      const int64_t idx = (int64_t)c * B + r;
+      stg(reinterpret_cast<floatx4*>(out + idx), o);
+      if (obf) stg4_h16(obf + idx, o, fmt);
     }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));
