@@ -129,41 +129,6 @@ __device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, float
   return part;
 }
 
-// Epilogue of a symmetric product without LDS (kDirect epilogues).  For each
-// group of four accumulators a lane holds rows r..r+3 of one column c: it
-// writes them there (on a diagonal tile only on and above the diagonal) and
-// writes the mirrored entries, columns r..r+3 of row c, with one vector
-// store (on a diagonal tile only those strictly below the diagonal).
-template <int TM, int TN, class Tile>
-__device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[TM][TN], int m0, int n0, int wm,
-                                                    int wn, int lane, bool diag) {
-  const int h = lane >> 5, cl = lane & 31;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
-        const int c = n0 + wn + 32 * j + cl;
-        floatx4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-        const floatx4 o = tile.value4(r, c, v);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (!diag || r + e <= c) tile.write(r + e, c, o[e]);
-        if (!diag || r + 3 < c) {
-          tile.write4t(c, r, o);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (r + e < c) tile.write(c, r + e, o[e]);
-        }
-      }
-    }
-}
-
 // Workgroup shapes of the 16-bit product.  The LDS traffic per MFMA falls
 // with the wave tile: 64 x 64 wave tiles read 1 KB of fragments per 32 x 32 x 16
 // MFMA, 64 x 128 ones 0.75 KB, and the 256 x 256 workgroup tile halves the
