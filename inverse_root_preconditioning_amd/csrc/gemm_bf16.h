@@ -44,7 +44,6 @@ struct H16Launch {
   int B;
   int tiles_n;
   int tiles_per_item;
-  int sym;
   uint32_t total;      // njobs * nitems * tiles_per_item
 };
 
@@ -159,7 +158,7 @@ __host__ __device__ constexpr int h16_tile_of(int B, bool sym) { return (!sym &&
 // are in registers while stage s is multiplied); the fragments of the next
 // 16-deep k step are read before the MFMAs of the current one, across the
 // stage boundary too.
-template <class Epi, int FMT, int CFG>
+template <class Epi, int FMT, int CFG, bool SYM>
 __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
     gemm_h16_nt_kernel(const H16Launch<Epi> P) {
   using S = H16Shape<CFG>;
@@ -177,7 +176,7 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
   const int64_t item = rem / P.tiles_per_item;
   int t = rem - (uint32_t)item * P.tiles_per_item;
   int tm, tn;
-  if (!P.sym) {
+  if constexpr (!SYM) {
     tm = t / P.tiles_n;
     tn = t - tm * P.tiles_n;
   } else {
@@ -205,7 +204,7 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
   // below the diagonal holds only entries that are never written: it skips
   // its fragment reads and MFMAs but still stages operands and meets every
   // barrier.
-  const bool active = CFG != H16_T128 || !(P.sym && tm == tn && wm >= wn + 32 * TN);
+  const bool active = CFG != H16_T128 || !(SYM && tm == tn && wm >= wn + 32 * TN);
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -287,12 +286,12 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
     constexpr int PH = (sizeof(lds) >= sizeof(float) * BM * (BN + 1)) ? 1 : 2;
     static_assert(sizeof(lds) >= sizeof(float) * (BM / PH) * (BN + 1), "LDS too small for the staging");
     part = staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn,
-                                                        lane, P.sym != 0, tm == tn);
+                                                        lane, SYM, tm == tn);
   } else {
-    if constexpr (Epi::kSym) {
+    if constexpr (Epi::kSym && SYM) {
       constexpr int PH = (sizeof(lds) >= sizeof(float) * BM * (BN + 1)) ? 1 : 2;
       static_assert(sizeof(lds) >= sizeof(float) * (BM / PH) * (BN + 1), "LDS too small for the transpose");
-      if (P.sym) {
+      {
         if constexpr (Epi::kDirect && !Epi::kReduce)
           sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn);
         else
@@ -300,7 +299,7 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
                                                                      n0, wm, wn, lane, tm == tn);
       }
     }
-    if (!(Epi::kSym && P.sym)) {
+    if constexpr (!(Epi::kSym && SYM)) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -318,7 +317,7 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
     const float tot = block_sum<NT>(part, red);
     if (threadIdx.x == 0) {
       tile.partial(tm * P.tiles_n + tn, tot);
-      if (P.sym && tm != tn) tile.partial(tn * P.tiles_n + tm, tot);  // the mirrored tile
+      if (SYM && tm != tn) tile.partial(tn * P.tiles_n + tm, tot);  // the mirrored tile
     }
   }
 }
@@ -417,6 +416,7 @@ template <class Epi>
 static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* bt, const typename Epi::Job* e,
                               int njobs, int64_t n, int B, bool sym, int fmt, hipStream_t st) {
   if (B % 128 != 0) return SHAMPOO_EUNSUPPORTED;
+  if (!Epi::kSym && sym) return SHAMPOO_EINVAL;  // no symmetric epilogue
   const int T = h16_tile_of(B, sym);
   H16Launch<Epi> P;
   memset(&P, 0, sizeof(P));
@@ -429,23 +429,31 @@ static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* b
   P.B = B;
   P.tiles_n = B / T;
   P.tiles_per_item = sym ? P.tiles_n * (P.tiles_n + 1) / 2 : P.tiles_n * P.tiles_n;
-  P.sym = sym ? 1 : 0;
   const uint64_t total = (uint64_t)njobs * n * P.tiles_per_item;
   if (total == 0) return SHAMPOO_OK;
   if (total > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
   P.total = (uint32_t)total;
-  if (T == 256) {
+  if (T == 256) {  // full products only
     constexpr int NT = H16Shape<H16_T256>::NT;
     if (fmt == H16_F16)
-      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16, H16_T256>), dim3(P.total), dim3(NT), 0, st, P);
+      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16, H16_T256, false>), dim3(P.total), dim3(NT), 0, st, P);
     else
-      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_BF16, H16_T256>), dim3(P.total), dim3(NT), 0, st, P);
+      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_BF16, H16_T256, false>), dim3(P.total), dim3(NT), 0, st, P);
   } else {
     constexpr int NT = H16Shape<H16_T128>::NT;
+    if constexpr (Epi::kSym) {
+      if (sym) {
+        if (fmt == H16_F16)
+          hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16, H16_T128, true>), dim3(P.total), dim3(NT), 0, st, P);
+        else
+          hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_BF16, H16_T128, true>), dim3(P.total), dim3(NT), 0, st, P);
+        return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMPOO_EHIP;
+      }
+    }
     if (fmt == H16_F16)
-      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16, H16_T128>), dim3(P.total), dim3(NT), 0, st, P);
+      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16, H16_T128, false>), dim3(P.total), dim3(NT), 0, st, P);
     else
-      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_BF16, H16_T128>), dim3(P.total), dim3(NT), 0, st, P);
+      hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_BF16, H16_T128, false>), dim3(P.total), dim3(NT), 0, st, P);
   }
   return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMPOO_EHIP;
 }

@@ -141,8 +141,7 @@ struct GemmLaunch {
   int64_t nitems;      // items per job
   int B;
   int tiles_n;         // B / BN
-  int tiles_per_item;  // tiles_m * tiles_n, or T (T + 1) / 2 when sym
-  int sym;             // product is symmetric: upper tiles only, mirrored stores
+  int tiles_per_item;  // tiles_m * tiles_n, or T (T + 1) / 2 for a symmetric product (upper tiles only)
   uint32_t total;      // njobs * nitems * tiles_per_item
 };
 
@@ -246,7 +245,9 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
     }
 }
 
-template <int TM, int TN, int LA, int LB, bool DA, bool DB, class Epi, int BK = kBK, int MINW = 2>
+// SYM: the product is symmetric (upper tiles only, see GemmLaunch::sym); a
+// template parameter so that each kernel carries only the epilogue it runs.
+template <int TM, int TN, int LA, int LB, bool DA, bool DB, class Epi, bool SYM, int BK = kBK, int MINW = 2>
 __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const GemmLaunch<Epi> P) {
   constexpr int BM = 64 * TM, BN = 64 * TN;
   using SA = Stager<BM, LA, DA, BK>;
@@ -263,7 +264,7 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   const int64_t item = rem / P.tiles_per_item;
   int t = rem - (uint32_t)item * P.tiles_per_item;
   int tm, tn;
-  if (!P.sym) {
+  if constexpr (!SYM) {
     tm = t / P.tiles_n;
     tn = t - tm * P.tiles_n;
   } else {  // upper-triangular tile enumeration, row by row
@@ -289,7 +290,7 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   // (rows 32 TM.., columns ..32 TN) holds only entries that are never
   // written: it skips its fragment reads and MFMAs (it still stages operands
   // and meets every barrier), which frees its SIMD for other workgroups.
-  const bool active = !(P.sym && tm == tn && wm > wn);
+  const bool active = !(SYM && tm == tn && wm > wn);
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -357,8 +358,8 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   typename Epi::Tile tile(P.e[job], item, P.B);
   float part = 0.f;
   bool done = false;
-  if constexpr (Epi::kSym) {
-    if (P.sym) {
+  if constexpr (Epi::kSym && SYM) {
+    {
       if constexpr (Epi::kDirect && !Epi::kReduce)
         sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn);
       else
@@ -383,7 +384,7 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
     const float tot = block_sum<kGemmThreads>(part, red);
     if (threadIdx.x == 0) {
       tile.partial(tm * P.tiles_n + tn, tot);
-      if (P.sym && tm != tn) tile.partial(tn * P.tiles_n + tm, tot);  // the mirrored tile
+      if (SYM && tm != tn) tile.partial(tn * P.tiles_n + tm, tot);  // the mirrored tile
     }
   }
 }

@@ -80,6 +80,7 @@ int gemm_tiles(int B) {
 template <int LA, int LB, bool DA, bool DB, class Epi>
 int run_gemm(const Operand* a, const Operand* b, const typename Epi::Job* e, int njobs, int64_t nitems,
              int B, bool sym, hipStream_t st, int fam = 0) {
+  if (!Epi::kSym && sym) return SHAMPOO_EINVAL;  // no symmetric epilogue
   GemmLaunch<Epi> P;
   memset(&P, 0, sizeof(P));
   for (int j = 0; j < njobs; ++j) {
@@ -92,16 +93,31 @@ int run_gemm(const Operand* a, const Operand* b, const typename Epi::Job* e, int
   P.B = B;
   P.tiles_n = B / T;
   P.tiles_per_item = sym ? P.tiles_n * (P.tiles_n + 1) / 2 : P.tiles_n * P.tiles_n;
-  P.sym = sym ? 1 : 0;
   const uint64_t total = (uint64_t)njobs * (uint64_t)nitems * (uint64_t)P.tiles_per_item;
   if (total == 0) return SHAMPOO_OK;
   if (total > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
   P.total = (uint32_t)total;
   timing_before(fam, st);
-  if (T == 128)
-    hipLaunchKernelGGL((gemm_f32_kernel<2, 2, LA, LB, DA, DB, Epi>), dim3(P.total), dim3(kGemmThreads), 0, st, P);
-  else
-    hipLaunchKernelGGL((gemm_f32_kernel<1, 1, LA, LB, DA, DB, Epi>), dim3(P.total), dim3(kGemmThreads), 0, st, P);
+  bool launched = false;
+  if constexpr (Epi::kSym) {
+    if (sym) {
+      if (T == 128)
+        hipLaunchKernelGGL((gemm_f32_kernel<2, 2, LA, LB, DA, DB, Epi, true>), dim3(P.total), dim3(kGemmThreads), 0,
+                           st, P);
+      else
+        hipLaunchKernelGGL((gemm_f32_kernel<1, 1, LA, LB, DA, DB, Epi, true>), dim3(P.total), dim3(kGemmThreads), 0,
+                           st, P);
+      launched = true;
+    }
+  }
+  if (!launched) {
+    if (T == 128)
+      hipLaunchKernelGGL((gemm_f32_kernel<2, 2, LA, LB, DA, DB, Epi, false>), dim3(P.total), dim3(kGemmThreads), 0,
+                         st, P);
+    else
+      hipLaunchKernelGGL((gemm_f32_kernel<1, 1, LA, LB, DA, DB, Epi, false>), dim3(P.total), dim3(kGemmThreads), 0,
+                         st, P);
+  }
   timing_after(fam, st);
   return check_launch();
 }
