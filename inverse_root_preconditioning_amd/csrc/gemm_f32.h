@@ -233,7 +233,7 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
         const floatx4 o = tile.value4(r, c, v);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (!diag || r + e <= c) tile.write(r + e, c, o[e]);
+          if (!diag || r + e <= c) tile.write_upper(r + e, c, o[e]);
         if (!diag || r + 3 < c) {
           tile.write4t(c, r, o);
         } else {
@@ -397,9 +397,10 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
 // write(row, col, o) for symmetric products; there the output at a mirrored
 // position is the value formed at the computed one, which assumes the other
 // inputs of the epilogue (an EMA state, Clenshaw terms) are symmetric too.
-// Those with kDirect also provide value4(r, c, v) for rows r..r+3 of column c
-// and write4t(c, r, o), which writes o to row c, columns r..r+3 (the
-// mirrored entries) with vector stores.
+// Those with kDirect also provide value4(r, c, v) for rows r..r+3 of column c,
+// write4t(c, r, o), which writes o to row c, columns r..r+3 (the mirrored
+// entries) with vector stores, and write_upper(row, col, o) for the computed
+// entries themselves.
 // ---------------------------------------------------------------------------
 
 // out = mult * acc + beta * cin (cin may alias out); X = I for a degenerate
@@ -460,6 +461,7 @@ struct EpiStore {
       if (out) stg(reinterpret_cast<floatx4*>(out + idx), o);
       if (o16) stg4_h16(o16 + idx, o, fmt);
     }
+    __device__ __forceinline__ void write_upper(int row, int col, float o) { write(row, col, o); }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));
       return 0.f;
@@ -622,7 +624,7 @@ struct EpiClenshaw {
     const float* b1;
     const float* b2;
     float cj, mult, k1, k2;
-    bool ident;
+    bool ident, is_final;
     int B;
     __device__ __forceinline__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
       const int64_t off = item * (int64_t)B_ * B_;
@@ -632,6 +634,7 @@ struct EpiClenshaw {
       b1 = j.b1 + off;
       b2 = j.b2 + off;
       cj = j.cj;
+      is_final = j.final != 0;
       if (j.final) {
         k1 = 2.f;
         k2 = 1.f;
@@ -674,6 +677,17 @@ struct EpiClenshaw {
       const int64_t idx = (int64_t)c * B + r;
       stg(reinterpret_cast<floatx4*>(out + idx), o);
       if (obf) stg4_h16(obf + idx, o, fmt);
+    }
+    // When the next product takes its operand from the 16-bit copy, an
+    // intermediate fp32 b is read back only at transposed positions (value4),
+    // i.e. on and below the diagonal, which the mirrored writes cover: its
+    // fp32 value above the diagonal is then not stored.  Without a 16-bit
+    // copy the fp32 b is the next product's operand and is stored in full,
+    // and so is the final X.
+    __device__ __forceinline__ void write_upper(int row, int col, float o) {
+      const int64_t idx = (int64_t)row * B + col;
+      if (obf == nullptr || is_final || row == col) stg(out + idx, o);
+      if (obf) stg(obf + idx, to_h16(o, fmt));
     }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));
