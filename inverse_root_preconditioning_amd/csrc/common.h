@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "../../include/shampoo.h"
 
 namespace shp {
@@ -38,6 +41,17 @@ __device__ __forceinline__ T ldg(const T* p) {
 template <class T>
 __device__ __forceinline__ void stg(T* p, const T& v) {
   *(__attribute__((address_space(1))) T*)p = v;
+}
+
+// f(std::integral_constant<int, i>) for i = 0..N-1, expanded at compile time
+// (indices stay constants even where a loop would be too large to unroll).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -151,7 +151,7 @@ struct H16Shape {
 // computed whole, which wastes more work on larger tiles, and their
 // epilogues (EMA and Clenshaw terms, mirrored writes) outweigh the main-loop
 // gain.
-__host__ __device__ constexpr int h16_tile_of(int B, bool sym) { return (!sym && B % 256 == 0) ? 256 : 128; }
+__host__ __device__ constexpr int h16_tile_of(int B, bool sym) { return (B % 256 == 0) ? 256 : 128; }
 
 // C_i = A_i Bt_i^T for 16-bit (bf16 or fp16) row-major stacks, fp32 accumulate.
 // k is staged kBK16 deep through two padded LDS buffers (loads of stage s + 1
@@ -204,7 +204,7 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
   // below the diagonal holds only entries that are never written: it skips
   // its fragment reads and MFMAs but still stages operands and meets every
   // barrier.
-  const bool active = CFG != H16_T128 || !(SYM && tm == tn && wm >= wn + 32 * TN);
+  const bool active = !(SYM && tm == tn && wm >= wn + 32 * TN);
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -285,8 +285,15 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
   if constexpr (CFG == H16_T256) {
     constexpr int PH = (sizeof(lds) >= sizeof(float) * BM * (BN + 1)) ? 1 : 2;
     static_assert(sizeof(lds) >= sizeof(float) * (BM / PH) * (BN + 1), "LDS too small for the staging");
-    part = staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn,
-                                                        lane, SYM, tm == tn);
+    constexpr bool kDirect = [] {
+      if constexpr (Epi::kSym) return Epi::kDirect && !Epi::kReduce && SYM;
+      return false;
+    }();
+    if constexpr (kDirect)
+      sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn);
+    else
+      part = staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm,
+                                                          wn, lane, SYM, tm == tn);
   } else {
     if constexpr (Epi::kSym && SYM) {
       constexpr int PH = (sizeof(lds) >= sizeof(float) * BM * (BN + 1)) ? 1 : 2;
@@ -433,8 +440,17 @@ static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* b
   if (total == 0) return SHAMPOO_OK;
   if (total > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
   P.total = (uint32_t)total;
-  if (T == 256) {  // full products only
+  if (T == 256) {
     constexpr int NT = H16Shape<H16_T256>::NT;
+    if constexpr (Epi::kSym) {
+      if (sym) {
+        if (fmt == H16_F16)
+          hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16, H16_T256, true>), dim3(P.total), dim3(NT), 0, st, P);
+        else
+          hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_BF16, H16_T256, true>), dim3(P.total), dim3(NT), 0, st, P);
+        return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMPOO_EHIP;
+      }
+    }
     if (fmt == H16_F16)
       hipLaunchKernelGGL((gemm_h16_nt_kernel<Epi, H16_F16, H16_T256, false>), dim3(P.total), dim3(NT), 0, st, P);
     else

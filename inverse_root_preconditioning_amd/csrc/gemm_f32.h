@@ -219,30 +219,23 @@ template <int TM, int TN, class Tile>
 __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[TM][TN], int m0, int n0, int wm,
                                                     int wn, int lane, bool diag) {
   const int h = lane >> 5, cl = lane & 31;
+  static_for<TM * TN * 4>([&](auto G) __attribute__((always_inline)) {
+    constexpr int i = decltype(G)::value / (TN * 4), j = (decltype(G)::value / 4) % TN, q = decltype(G)::value % 4;
+    const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
+    const int c = n0 + wn + 32 * j + cl;
+    const floatx4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+    const floatx4 o = tile.value4(r, c, v);
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int e = 0; e < 4; ++e)
+      if (!diag || r + e <= c) tile.write_upper(r + e, c, o[e]);
+    if (!diag || r + 3 < c) {
+      tile.write4t(c, r, o);
+    } else {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
-        const int c = n0 + wn + 32 * j + cl;
-        floatx4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e];
-        const floatx4 o = tile.value4(r, c, v);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (!diag || r + e <= c) tile.write_upper(r + e, c, o[e]);
-        if (!diag || r + 3 < c) {
-          tile.write4t(c, r, o);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (r + e < c) tile.write(c, r + e, o[e]);
-        }
-      }
+      for (int e = 0; e < 4; ++e)
+        if (r + e < c) tile.write(c, r + e, o[e]);
     }
+  });
 }
 
 // SYM: the product is symmetric (upper tiles only, see GemmLaunch::sym); a
