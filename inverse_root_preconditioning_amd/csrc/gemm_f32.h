@@ -284,6 +284,9 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   // written: it skips its fragment reads and MFMAs (it still stages operands
   // and meets every barrier), which frees its SIMD for other workgroups.
   const bool active = !(SYM && tm == tn && wm > wn);
+  // ... and a wave on the diagonal skips its 32 x 32 blocks that lie wholly
+  // below it (block (i, j) when wm + 32 i >= wn + 32 j + 32).
+  const bool dtile = SYM && tm == tn;
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -335,7 +338,8 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
           for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
+              if (!(dtile && wm + 32 * i >= wn + 32 * j + 32))
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
       }
     }
     if (s + 1 < nstages) {
