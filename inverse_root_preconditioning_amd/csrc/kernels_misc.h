@@ -155,22 +155,29 @@ __global__ void __launch_bounds__(256, 2) pi_step_kernel(const PiArgs P) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 
-  SA sa;
-  SV sv;
+  // Two register sets keep the loads of stages s + 1 and s + 2 in flight
+  // while stage s is multiplied (the kernel streams F once; the MFMA work is
+  // small), two LDS buffers hold stages s and s + 1.
+  SA sa[2];
+  SV sv[2];
   const int stage = SA::kFloats + SV::kFloats;
   const int nstages = P.B / BK;
-  sa.load(va, m0, 0);
-  sv.load(vv, 0, 0);
-  sa.store(lds);
-  sv.store(lds + SA::kFloats);
+  sa[0].load(va, m0, 0);
+  sv[0].load(vv, 0, 0);
+  if (nstages > 1) {
+    sa[1].load(va, m0, BK);
+    sv[1].load(vv, 0, BK);
+  }
+  sa[0].store(lds);
+  sv[0].store(lds + SA::kFloats);
   __syncthreads();
-  for (int s = 0; s < nstages; ++s) {
-    const int cur = s & 1;
+  auto step = [&](auto cur_c, int s) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_c)::value;
     float* bufA = lds + cur * stage;
     float* bufV = bufA + SA::kFloats;
-    if (s + 1 < nstages) {
-      sa.load(va, m0, (s + 1) * BK);
-      sv.load(vv, 0, (s + 1) * BK);
+    if (s + 2 < nstages) {  // set `cur` was stored at the previous step: reuse it for stage s + 2
+      sa[cur].load(va, m0, (s + 2) * BK);
+      sv[cur].load(vv, 0, (s + 2) * BK);
     }
 #pragma unroll
     for (int gg = 0; gg < BK / 8 / KS; ++gg) {
@@ -182,10 +189,14 @@ __global__ void __launch_bounds__(256, 2) pi_step_kernel(const PiArgs P) {
     }
     if (s + 1 < nstages) {
       float* nA = lds + (cur ^ 1) * stage;
-      sa.store(nA);
-      sv.store(nA + SA::kFloats);
+      sa[cur ^ 1].store(nA);
+      sv[cur ^ 1].store(nA + SA::kFloats);
     }
     __syncthreads();
+  };
+  for (int s = 0; s < nstages; s += 2) {
+    step(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < nstages) step(std::integral_constant<int, 1>{}, s + 1);
   }
 
   if (KS > 1) {  // waves with ks > 0 hand their partial sums to ks == 0 (lds is free now)
