@@ -197,7 +197,7 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
   const uint16_t* Bt = (job == 0 ? P.bt[0] : P.bt[1]) + off;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = (wave / WC) * 32 * TM, wn = (wave % WC) * 32 * TN;
   const int rr = lane & 31, h = lane >> 5;
   // On a diagonal tile of a symmetric product a wave whose block lies wholly

@@ -276,7 +276,9 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   const OperandView vb = operand_view(P.b[job], item, P.B);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The wave index is uniform across the wave; readfirstlane lets the compiler
+  // see that, so tests on it become scalar branches rather than exec masking.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = (wave >> 1) * 32 * TM;  // wave's row offset inside the tile
   const int wn = (wave & 1) * 32 * TN;
   // On a diagonal tile of a symmetric product the wave below the diagonal
@@ -284,9 +286,11 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   // written: it skips its fragment reads and MFMAs (it still stages operands
   // and meets every barrier), which frees its SIMD for other workgroups.
   const bool active = !(SYM && tm == tn && wm > wn);
-  // ... and a wave on the diagonal skips its 32 x 32 blocks that lie wholly
-  // below it (block (i, j) when wm + 32 i >= wn + 32 j + 32).
-  const bool dtile = SYM && tm == tn;
+  // ... and a wave on the diagonal (wm == wn; the wave tiles are square) skips
+  // its 32 x 32 blocks (i, j), i > j, which lie wholly below it.  The k-loop
+  // body is instantiated for both cases, so the MFMA stream has no branches.
+  static_assert(TM == TN, "square wave tiles");
+  const bool skip_low = SYM && tm == tn && wm == wn;
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -307,48 +311,58 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   sb.store(lds + SA::kFloats);
   __syncthreads();
 
-  for (int s = 0; s < nstages; ++s) {
-    const int cur = s & 1;
-    const float* bufA = lds + cur * kStage;
-    const float* bufB = bufA + SA::kFloats;
-    if (s + 1 < nstages) {
-      sa.load(va, m0, (s + 1) * BK);
-      sb.load(vb, n0, (s + 1) * BK);
-    }
-    // Fragments are double-buffered in registers: the reads for k-group g+1
-    // are issued before the MFMAs of group g, so LDS latency hides behind them.
-    if (active) {
-      floatx4 fa[2][TM], fb[2][TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) fa[0][i] = SA::frag(bufA, wm + 32 * i, 0, lane);
-#pragma unroll
-      for (int j = 0; j < TN; ++j) fb[0][j] = SB::frag(bufB, wn + 32 * j, 0, lane);
-#pragma unroll
-      for (int g = 0; g < BK / 8; ++g) {
-        const int c = g & 1;
-        if (g + 1 < BK / 8) {
-#pragma unroll
-          for (int i = 0; i < TM; ++i) fa[c ^ 1][i] = SA::frag(bufA, wm + 32 * i, g + 1, lane);
-#pragma unroll
-          for (int j = 0; j < TN; ++j) fb[c ^ 1][j] = SB::frag(bufB, wn + 32 * j, g + 1, lane);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              if (!(dtile && wm + 32 * i >= wn + 32 * j + 32))
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
+  // The whole stage loop is instantiated for both block-skip cases, so the
+  // MFMA stream carries no branches and the accumulators stay in place.
+  auto mainloop = [&](auto skip) __attribute__((always_inline)) {
+    constexpr bool kSkip = decltype(skip)::value;
+    for (int s = 0; s < nstages; ++s) {
+      const int cur = s & 1;
+      const float* bufA = lds + cur * kStage;
+      const float* bufB = bufA + SA::kFloats;
+      if (s + 1 < nstages) {
+        sa.load(va, m0, (s + 1) * BK);
+        sb.load(vb, n0, (s + 1) * BK);
       }
+      // Fragments are double-buffered in registers: the reads for k-group
+      // g+1 are issued before the MFMAs of group g, so LDS latency hides
+      // behind them.
+      if (active) {
+        floatx4 fa[2][TM], fb[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[0][i] = SA::frag(bufA, wm + 32 * i, 0, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[0][j] = SB::frag(bufB, wn + 32 * j, 0, lane);
+#pragma unroll
+        for (int g = 0; g < BK / 8; ++g) {
+          const int c = g & 1;
+          if (g + 1 < BK / 8) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[c ^ 1][i] = SA::frag(bufA, wm + 32 * i, g + 1, lane);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb[c ^ 1][j] = SB::frag(bufB, wn + 32 * j, g + 1, lane);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int j = 0; j < TN; ++j)
+                if (!kSkip || i <= j)
+                  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
+        }
+      }
+      if (s + 1 < nstages) {
+        float* nxt = lds + (cur ^ 1) * kStage;
+        sa.store(nxt);
+        sb.store(nxt + SA::kFloats);
+      }
+      __syncthreads();
     }
-    if (s + 1 < nstages) {
-      float* nxt = lds + (cur ^ 1) * kStage;
-      sa.store(nxt);
-      sb.store(nxt + SA::kFloats);
-    }
-    __syncthreads();
-  }
+  };
+  if (SYM && skip_low)
+    mainloop(std::true_type{});
+  else
+    mainloop(std::false_type{});
 
   // Epilogue.  Accumulator e of block (i, j) sits at
   // row = 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = 32 j + lane % 32.
