@@ -238,6 +238,73 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
   });
 }
 
+// Workgroup lid -> (job, item, tile row tm, tile column tn); a symmetric
+// product enumerates only its upper tiles (tm <= tn), row by row.
+template <bool SYM, class Epi>
+__device__ __forceinline__ void decode_tile(const GemmLaunch<Epi>& P, uint32_t lid, int& job, int64_t& item, int& tm,
+                                            int& tn) {
+  const uint32_t per_job = (uint32_t)P.nitems * P.tiles_per_item;
+  job = lid / per_job;
+  const uint32_t rem = lid - job * per_job;
+  item = rem / P.tiles_per_item;
+  int t = rem - (uint32_t)item * P.tiles_per_item;
+  if constexpr (!SYM) {
+    tm = t / P.tiles_n;
+    tn = t - tm * P.tiles_n;
+  } else {
+    tm = 0;
+    int rowlen = P.tiles_n;
+    while (t >= rowlen) {
+      t -= rowlen;
+      ++tm;
+      --rowlen;
+    }
+    tn = tm + t;
+  }
+}
+
+// Epilogue of one output tile.  Accumulator e of block (i, j) sits at
+// row = 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = 32 j + lane % 32 of the
+// wave's (32 TM) x (32 TN) part, at (wm, wn) in the tile at (m0, n0).  `lds`
+// must hold (BM / PH) x (BN + 1) floats and be free; `red` NT / 64 floats.
+template <int TM, int TN, int BM, int BN, int NT, int PH, bool SYM, class Epi>
+__device__ __forceinline__ void gemm_epilogue(const GemmLaunch<Epi>& P, int job, int64_t item, int tm, int tn,
+                                              floatx16 (&acc)[TM][TN], float* lds, float* red, int m0, int n0,
+                                              int wm, int wn, int lane) {
+  typename Epi::Tile tile(P.e[job], item, P.B);
+  float part = 0.f;
+  bool done = false;
+  if constexpr (Epi::kSym && SYM) {
+    if constexpr (Epi::kDirect && !Epi::kReduce)
+      sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn);
+    else
+      part = sym_epilogue<TM, TN, BM, BN, NT, PH, Epi::kReduce>(tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
+    done = true;
+  }
+  if (!done) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int col = n0 + wn + 32 * j + (lane & 31);
+          part += tile.store(row, col, acc[i][j][e]);
+        }
+        // one 32 x 32 block at a time: the epilogue's own loads need few registers
+        if constexpr (NT > kGemmThreads) __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+  if constexpr (Epi::kReduce) {
+    const float tot = block_sum<NT>(part, red);
+    if (threadIdx.x == 0) {
+      tile.partial(tm * P.tiles_n + tn, tot);
+      if (SYM && tm != tn) tile.partial(tn * P.tiles_n + tm, tot);  // the mirrored tile
+    }
+  }
+}
+
 // SYM: the product is symmetric (upper tiles only, see GemmLaunch::sym); a
 // template parameter so that each kernel carries only the epilogue it runs.
 template <int TM, int TN, int LA, int LB, bool DA, bool DB, class Epi, bool SYM, int BK = kBK, int MINW = 2>
@@ -250,26 +317,9 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   __shared__ __attribute__((aligned(16))) float lds[kPipe > kTrans ? kPipe : kTrans];
   __shared__ float red[kGemmThreads / kWave];
 
-  const uint32_t lid = xcd_remap(blockIdx.x, P.total);
-  const uint32_t per_job = (uint32_t)P.nitems * P.tiles_per_item;
-  const int job = lid / per_job;
-  const uint32_t rem = lid - job * per_job;
-  const int64_t item = rem / P.tiles_per_item;
-  int t = rem - (uint32_t)item * P.tiles_per_item;
-  int tm, tn;
-  if constexpr (!SYM) {
-    tm = t / P.tiles_n;
-    tn = t - tm * P.tiles_n;
-  } else {  // upper-triangular tile enumeration, row by row
-    tm = 0;
-    int rowlen = P.tiles_n;
-    while (t >= rowlen) {
-      t -= rowlen;
-      ++tm;
-      --rowlen;
-    }
-    tn = tm + t;
-  }
+  int job, tm, tn;
+  int64_t item;
+  decode_tile<SYM>(P, xcd_remap(blockIdx.x, P.total), job, item, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const OperandView va = operand_view(P.a[job], item, P.B);
@@ -364,40 +414,164 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
   else
     mainloop(std::false_type{});
 
-  // Epilogue.  Accumulator e of block (i, j) sits at
-  // row = 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = 32 j + lane % 32.
-  typename Epi::Tile tile(P.e[job], item, P.B);
-  float part = 0.f;
-  bool done = false;
-  if constexpr (Epi::kSym && SYM) {
-    {
-      if constexpr (Epi::kDirect && !Epi::kReduce)
-        sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn);
-      else
-        part = sym_epilogue<TM, TN, BM, BN, kGemmThreads, kPipe >= BM * (BN + 1) ? 1 : 2, Epi::kReduce>(
-            tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
-      done = true;
-    }
+  gemm_epilogue<TM, TN, BM, BN, kGemmThreads, kPipe >= BM * (BN + 1) ? 1 : 2, SYM>(P, job, item, tm, tn, acc, lds,
+                                                                                    red, m0, n0, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Large tiles for dense operands (A with k contiguous, B with n contiguous,
+// B a multiple of 256): 256 x 256 output tiles, 16 waves of 64 x 64 each, one
+// workgroup per CU.  Each thread moves one 16-byte piece of A and one of B
+// per k-stage straight into LDS (global_load_lds_dwordx4: lane l of a wave
+// writes 16 bytes at the wave's LDS base + 16 l), through a ring of three
+// stages, so loads run two stages ahead of the MFMAs and a stage ends with a
+// wait for the next stage's loads only, then one barrier.  Twice the tile
+// edge halves the operand traffic per flop of the 128 x 128 kernel.
+//
+// LDS layout of a stage: A as [row][4 quads of 4 k], the quad index XOR-ed
+// with (row >> 1) & 3 so that the 16-byte fragment reads of 8 consecutive
+// rows hit 8 different bank groups; B as [k][256] (fragment reads run along
+// n, conflict free).  Every stage issues its loads, past the last stage again
+// the last one into the free buffer, so the count of loads in flight, and
+// hence each wait, is the same on every path.
+//
+// Waves are placed on the 4 x 4 grid of 64 x 64 blocks so that on a diagonal
+// tile of a symmetric product (6 blocks idle below the diagonal, 4 on it at
+// three quarters of the work) each SIMD (wave % 4, assuming the dispatcher
+// deals waves round-robin) carries at most 2.5 blocks of work instead of 3.75.
+// ---------------------------------------------------------------------------
+constexpr int kBigThreads = 1024;
+constexpr int kBigTile = 256;
+// block (row, col) of wave w: 4 bits r * 4 + c per wave, w = 0 in the low bits
+constexpr uint64_t kBigPlace = 0x9CDEF584A07B6321ull;
+
+template <class Epi, bool SYM>
+__global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const GemmLaunch<Epi> P) {
+  constexpr int TM = 2, TN = 2, BM = kBigTile, BN = kBigTile, BK = 16, NT = kBigThreads;
+  constexpr int kA = BM * BK, kStage = kA + BK * BN;  // floats
+  constexpr int PH = 4;                                // phases of the symmetric epilogue's transpose
+  static_assert((BM / PH) * (BN + 1) <= 3 * kStage, "transpose fits the ring");
+  static_assert(BM * BK / 4 == NT && BK * BN / 4 == NT, "one 16-byte piece of A and of B per thread");
+  __shared__ __attribute__((aligned(16))) float lds[3 * kStage];
+  __shared__ float red[NT / kWave];
+
+  int job, tm, tn;
+  int64_t item;
+  decode_tile<SYM>(P, xcd_remap(blockIdx.x, P.total), job, item, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int B = P.B;
+  const float* pa = P.a[job].base + item * (int64_t)B * B;
+  const float* pb = P.b[job].base + item * (int64_t)B * B;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int place = (int)((kBigPlace >> (4 * wave)) & 15);
+  const int wm = (place >> 2) * 64, wn = (place & 3) * 64;
+  const bool active = !(SYM && tm == tn && wm > wn);
+  const bool skip_low = SYM && tm == tn && wm == wn;
+
+  // this thread's pieces: A row r, quad q (stored at quad q ^ swz); B row k, columns 4 nq..
+  const float* srcA;
+  const float* srcB;
+  {
+    const int r = tid >> 2, qs = tid & 3, qg = qs ^ ((r >> 1) & 3);
+    srcA = pa + (int64_t)(m0 + r) * B + 4 * qg;
+    const int k = tid >> 6, nq = tid & 63;
+    srcB = pb + (int64_t)k * B + n0 + 4 * nq;
   }
-  if (!done) {
+  const int nstages = B / BK;
+  const int wbase = wave * 64 * 4;  // this wave's 1 KB of each operand region
+  auto issue = [&](float* __restrict__ buf, int s) __attribute__((always_inline)) {
+    const int k0 = min(s, nstages - 1) * BK;
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcA + k0),
+                                     (__attribute__((address_space(3))) void*)(buf + wbase), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcB + (int64_t)k0 * B),
+                                     (__attribute__((address_space(3))) void*)(buf + kA + wbase), 16, 0, 0);
+  };
+  // s_waitcnt immediates: vmcnt(2) (the newest stage's two loads stay in flight) or vmcnt(0), with lgkmcnt(0)
+  constexpr int kWaitAhead = 2 | (7 << 4);
+  constexpr int kWaitAll = 0 | (7 << 4);
+
+  floatx16 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = m0 + wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          const int col = n0 + wn + 32 * j + (lane & 31);
-          part += tile.store(row, col, acc[i][j][e]);
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  float* const b0 = lds;
+  float* const b1 = lds + kStage;
+  float* const b2 = lds + 2 * kStage;
+  issue(b0, 0);
+  issue(b1, 1);
+  __builtin_amdgcn_s_waitcnt(kWaitAhead);
+  __builtin_amdgcn_s_barrier();
+
+  auto mainloop = [&](auto skip) __attribute__((always_inline)) {
+    constexpr bool kSkip = decltype(skip)::value;
+    // One stage: loads for stage s + 2 into `wr`, MFMAs on `rd` (stage s).
+    auto step = [&](const float* __restrict__ rd, float* __restrict__ wr, int s) __attribute__((always_inline)) {
+      issue(wr, s + 2);
+      if (active) {
+        auto fragA = [&](int i, int g) __attribute__((always_inline)) {
+          const int row = wm + 32 * i + (lane & 31), quad = 2 * g + (lane >> 5);
+          return *reinterpret_cast<const floatx4*>(rd + 4 * (row * 4 + (quad ^ ((row >> 1) & 3))));
+        };
+        auto fragB = [&](int j, int g) __attribute__((always_inline)) {
+          const float* q = rd + kA + (g * 8 + (lane >> 5) * 4) * BN + wn + 32 * j + (lane & 31);
+          floatx4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = q[e * BN];
+          return x;
+        };
+        floatx4 fa[2][TM], fb[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[0][i] = fragA(i, 0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[0][j] = fragB(j, 0);
+#pragma unroll
+        for (int g = 0; g < BK / 8; ++g) {
+          const int c = g & 1;
+          if (g + 1 < BK / 8) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) fa[c ^ 1][i] = fragA(i, g + 1);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) fb[c ^ 1][j] = fragB(j, g + 1);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int j = 0; j < TN; ++j)
+                if (!kSkip || i <= j)
+                  acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
         }
-  }
-  if constexpr (Epi::kReduce) {
-    const float tot = block_sum<kGemmThreads>(part, red);
-    if (threadIdx.x == 0) {
-      tile.partial(tm * P.tiles_n + tn, tot);
-      if (SYM && tm != tn) tile.partial(tn * P.tiles_n + tm, tot);  // the mirrored tile
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitAhead);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    int s = 0;
+    for (; s + 3 <= nstages; s += 3) {
+      step(b0, b2, s);
+      step(b1, b0, s + 1);
+      step(b2, b1, s + 2);
     }
-  }
+    if (s < nstages) step(b0, b2, s);
+    if (s + 1 < nstages) step(b1, b0, s + 1);
+  };
+  if (SYM && skip_low)
+    mainloop(std::true_type{});
+  else
+    mainloop(std::false_type{});
+  // drain the loads issued past the last stage before the epilogue reuses LDS
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __syncthreads();
+
+  gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM>(P, job, item, tm, tn, acc, lds, red, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -421,6 +595,8 @@ struct EpiStore {
   static constexpr bool kReduce = false;
   static constexpr bool kSym = true;
   static constexpr bool kDirect = true;
+  // gemm_f32_big_kernel fits 128 VGPRs without spilling (symmetric / full)
+  static constexpr bool kBigSym = true, kBigFull = false;
   struct Job {
     float* out;          // fp32 output (may be null when only the 16-bit copy is needed)
     const float* cin;
@@ -487,6 +663,7 @@ struct EpiPair : EpiStore {};
 
 // Output through a block descriptor: only rows x cols of the block is written.
 struct EpiStoreDesc {
+  static constexpr bool kBigSym = false, kBigFull = true;
   static constexpr bool kSym = false;
   static constexpr bool kReduce = false;
   struct Job {
@@ -519,6 +696,7 @@ struct EpiStoreDesc {
 struct EpiNdbE {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = false;
+  static constexpr bool kBigSym = false, kBigFull = true;
   static constexpr bool kReduce = true;
   struct Job {
     float* e;
@@ -555,6 +733,7 @@ struct EpiNdbE {
 struct EpiCnM {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = false;
+  static constexpr bool kBigSym = false, kBigFull = false;
   static constexpr bool kReduce = true;
   struct Job {
     float* m;            // fp32 outputs (null: not written)
@@ -616,6 +795,7 @@ struct EpiClenshaw {
   static constexpr bool kReduce = false;
   static constexpr bool kSym = true;
   static constexpr bool kDirect = true;
+  static constexpr bool kBigSym = true, kBigFull = false;
   struct Job {
     float* out;
     uint16_t* out16;     // optional 16-bit copy of b (operand of the next product)

@@ -69,7 +69,24 @@ int ew_chunks(int B) {
   return (int)c;
 }
 
-int gemm_tiles(int B) {
+// Output tile edge of an fp32 product: gemm_f32_big_kernel (256) for dense
+// operands when B is a multiple of 256 and the epilogue fits that kernel's
+// register budget, else 128 or 64.
+template <class Epi>
+int f32_tile_edge(int B, bool sym, bool dense) {
+  const bool fits = sym ? Epi::kBigSym : Epi::kBigFull;
+  return (dense && fits && B % kBigTile == 0) ? kBigTile : tile_of(B);
+}
+
+// Tile count (reduction partials per item) of a product of dense stacks.
+template <class Epi>
+int f32_tiles(int B, bool sym) {
+  const int t = B / f32_tile_edge<Epi>(B, sym, true);
+  return t * t;
+}
+
+// The most tiles any fp32 product of size B uses (workspace sizing).
+int gemm_tiles_max(int B) {
   const int t = B / tile_of(B);
   return t * t;
 }
@@ -88,7 +105,8 @@ int run_gemm(const Operand* a, const Operand* b, const typename Epi::Job* e, int
     P.b[j] = b[j];
     P.e[j] = e[j];
   }
-  const int T = tile_of(B);
+  const int T = f32_tile_edge<Epi>(B, sym, LA == KCONTIG && LB == MNCONTIG && !DA && !DB);
+  const bool big = T == kBigTile;
   P.nitems = nitems;
   P.B = B;
   P.tiles_n = B / T;
@@ -99,8 +117,25 @@ int run_gemm(const Operand* a, const Operand* b, const typename Epi::Job* e, int
   P.total = (uint32_t)total;
   timing_before(fam, st);
   bool launched = false;
+  if constexpr (LA == KCONTIG && LB == MNCONTIG && !DA && !DB) {
+    if (big) {
+      if constexpr (Epi::kSym && Epi::kBigSym) {
+        if (sym) {
+          hipLaunchKernelGGL((gemm_f32_big_kernel<Epi, true>), dim3(P.total), dim3(kBigThreads), 0, st, P);
+          launched = true;
+        }
+      }
+      if constexpr (Epi::kBigFull) {
+        if (!sym) {
+          hipLaunchKernelGGL((gemm_f32_big_kernel<Epi, false>), dim3(P.total), dim3(kBigThreads), 0, st, P);
+          launched = true;
+        }
+      }
+      if (!launched) return SHAMPOO_EUNSUPPORTED;  // unreachable: f32_tile_edge chose this kernel
+    }
+  }
   if constexpr (Epi::kSym) {
-    if (sym) {
+    if (sym && !launched) {
       if (T == 128)
         hipLaunchKernelGGL((gemm_f32_kernel<2, 2, LA, LB, DA, DB, Epi, true>), dim3(P.total), dim3(kGemmThreads), 0,
                            st, P);
@@ -220,7 +255,7 @@ size_t cn16_layout(Carver& c, int64_t nf, int B, Cn16Ws* out) {
     w.pool.buf[i] = c.take<uint16_t>(stack_elems(nf, B));
     w.pool.used[i] = false;
   }
-  const int cnt = gemm_tiles(B) > ew_chunks(B) ? gemm_tiles(B) : ew_chunks(B);
+  const int cnt = gemm_tiles_max(B) > ew_chunks(B) ? gemm_tiles_max(B) : ew_chunks(B);
   w.partials = c.take<float>((size_t)nf * cnt);
   if (out) *out = w;
   return c.off;
@@ -235,7 +270,7 @@ size_t newton_layout(Carver& c, int64_t nf, int B, int variant, NewtonWs* out) {
     w.pool.buf[i] = c.take<float>(stack_elems(nf, B));
     w.pool.used[i] = false;
   }
-  const int cnt = gemm_tiles(B) > ew_chunks(B) ? gemm_tiles(B) : ew_chunks(B);
+  const int cnt = gemm_tiles_max(B) > ew_chunks(B) ? gemm_tiles_max(B) : ew_chunks(B);
   w.partials = c.take<float>((size_t)nf * cnt);
   if (out) *out = w;
   return c.off;
@@ -425,7 +460,7 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
   SHP_TRY(run_ew<EW_NDB_START>(a, nf, c.st));
   SHP_TRY(run_resid(c.ws->partials, a.chunks, c.resid, c.ncols, pass * c.iters, c.status, nf, c.st));
 
-  const int tiles = gemm_tiles(B);
+  const int tiles = f32_tiles<EpiNdbE>(B, c.sym_p);
   float* Z = E;  // Z_1 = E_0 (Z_0 = I)
   // Iteration 1: Y_1 = Y_0 E_0.
   if (c.iters == 1) {
@@ -582,7 +617,7 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
     s.chunks = ew_chunks(B);
     return run_ew<EW_SCALE_COPY>(s, nf, st);
   }
-  const int tiles = gemm_tiles(B);
+  const int tiles = f32_tiles<EpiCnM>(B, sym_c);
   float* X = nullptr;  // X_1 = C_0 (X_0 = I): first iteration has no X product
   for (int it = 0; it < iters; ++it) {
     const bool last = (it == iters - 1);
