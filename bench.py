@@ -241,8 +241,13 @@ def main(argv=None):
     # (the default for these launches) needs only its upper triangle with the
     # diagonal, B (B + 1) / 2 entries of 2 B flops each.
     sym_product = float(B) * B * (B + 1)
-    tiles = B // 128 if B % 128 == 0 else B // 64
-    executed = 2.0 * B ** 3 * (tiles * (tiles + 1) / 2) / tiles ** 2  # upper tiles incl. the diagonal ones
+    # MFMA work a symmetric fp32 product executes: the off-diagonal upper tiles
+    # in full and, of each diagonal tile, the 32 x 32 blocks its active waves
+    # compute (256 tiles: 9/16 of the tile; 128 tiles: 10/16; 64 tiles: 3/4).
+    edge, diag_frac = (256, 9 / 16) if B % 256 == 0 else (128, 10 / 16) if B % 128 == 0 else (64, 3 / 4)
+    tiles = B // edge
+    executed = 2.0 * B ** 3 * (tiles * (tiles - 1) / 2 + tiles * diag_frac) / tiles ** 2
+    f32_kernel = "gemm_f32_big_kernel" if edge == 256 else "gemm_f32_kernel"
     base_variant = cfg.variant & 0xff  # without the modifier bits
     if cfg.solver == "newton" and base_variant in (capi.CN, capi.CN_F16):
         family, per_step = capi.TIME_CN_M, cfg.iters - 1
@@ -256,7 +261,7 @@ def main(argv=None):
         family, per_step = capi.TIME_NDB_PAIR, 2 * (cfg.iters - 2)
         flops_per_launch = 2 * nf * sym_product
         mfma_flops = 2 * nf * executed
-        peak, kname = PEAK_F32_MFMA, ("gemm_f32_kernel<EpiPair> (Newton-DB Y E and E Z, 2 symmetric products "
+        peak, kname = PEAK_F32_MFMA, (f32_kernel + "<EpiPair> (Newton-DB Y E and E Z, 2 symmetric products "
                                       "per factor, upper tiles)")
     else:
         family, per_step = capi.TIME_CLENSHAW, cfg.degree - 1
@@ -264,7 +269,7 @@ def main(argv=None):
         mfma_flops = nf * executed
         bf = cfg.prec == capi.BF16_IN
         peak = PEAK_BF16_MFMA if bf else PEAK_F32_MFMA
-        kname = ("gemm_h16_nt_kernel<EpiClenshaw, bf16>" if bf else "gemm_f32_kernel<EpiClenshaw>") + \
+        kname = ("gemm_h16_nt_kernel<EpiClenshaw, bf16>" if bf else f32_kernel + "<EpiClenshaw>") + \
             " (one symmetric Clenshaw product per factor, upper tiles)"
     cap = max(1, per_step * refreshes)
     kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]

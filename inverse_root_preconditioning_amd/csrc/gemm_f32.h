@@ -238,16 +238,19 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
   });
 }
 
-// Workgroup lid -> (job, item, tile row tm, tile column tn); a symmetric
-// product enumerates only its upper tiles (tm <= tn), row by row.
+// Workgroup lid -> (job, item, tile row tm, tile column tn), item-major: the
+// tiles of both jobs of one item are neighbours, so that the workgroups that
+// run together share that item's operands (E in Y E and E Z) through L2.  A
+// symmetric product enumerates only its upper tiles (tm <= tn), row by row.
 template <bool SYM, class Epi>
 __device__ __forceinline__ void decode_tile(const GemmLaunch<Epi>& P, uint32_t lid, int& job, int64_t& item, int& tm,
                                             int& tn) {
-  const uint32_t per_job = (uint32_t)P.nitems * P.tiles_per_item;
-  job = lid / per_job;
-  const uint32_t rem = lid - job * per_job;
-  item = rem / P.tiles_per_item;
-  int t = rem - (uint32_t)item * P.tiles_per_item;
+  const uint32_t tpi = (uint32_t)P.tiles_per_item;
+  const uint32_t njobs = P.total / ((uint32_t)P.nitems * tpi);
+  item = lid / (njobs * tpi);
+  const uint32_t rem = lid - (uint32_t)item * njobs * tpi;
+  job = rem / tpi;
+  int t = rem - job * tpi;
   if constexpr (!SYM) {
     tm = t / P.tiles_n;
     tn = t - tm * P.tiles_n;
