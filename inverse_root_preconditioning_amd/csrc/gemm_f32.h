@@ -427,8 +427,8 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
 // workgroup per CU.  Each thread moves one 16-byte piece of A and one of B
 // per k-stage straight into LDS (global_load_lds_dwordx4: lane l of a wave
 // writes 16 bytes at the wave's LDS base + 16 l), through a ring of three
-// stages, so loads run two stages ahead of the MFMAs and a stage ends with a
-// wait for the next stage's loads only, then one barrier.  Twice the tile
+// stages: the loads for stage s + 2 leave at the end of stage s, and a stage
+// ends with a wait for the next stage's loads only, then one barrier.  Twice the tile
 // edge halves the operand traffic per flop of the 128 x 128 kernel.
 //
 // LDS layout of a stage: A as [row][4 quads of 4 k], the quad index XOR-ed
@@ -453,10 +453,13 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
   constexpr int TM = 2, TN = 2, BM = kBigTile, BN = kBigTile, BK = 16, NT = kBigThreads;
   constexpr int kA = BM * BK, kStage = kA + BK * BN;  // floats
   constexpr int PH = 4;                                // phases of the symmetric epilogue's transpose
-  static_assert((BM / PH) * (BN + 1) <= 3 * kStage, "transpose fits the ring");
+  static_assert((BM / PH) * (BN + 1) + NT / kWave <= 3 * kStage, "transpose and reduction fit the ring");
   static_assert(BM * BK / 4 == NT && BK * BN / 4 == NT, "one 16-byte piece of A and of B per thread");
+  // One LDS object only: with a second one (a separate reduction array) the
+  // compiler no longer tells the ring's buffers apart and waits for every
+  // load in flight before each LDS read.
   __shared__ __attribute__((aligned(16))) float lds[3 * kStage];
-  __shared__ float red[NT / kWave];
+  float* const red = lds + 3 * kStage - NT / kWave;  // past the epilogue's transpose
 
   int job, tm, tn;
   int64_t item;
@@ -513,9 +516,12 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
 
   auto mainloop = [&](auto skip) __attribute__((always_inline)) {
     constexpr bool kSkip = decltype(skip)::value;
-    // One stage: loads for stage s + 2 into `wr`, MFMAs on `rd` (stage s).
+    // One stage: MFMAs on `rd` (stage s), then the loads for stage s + 2 into
+    // `wr`.  The loads are issued after this stage's LDS reads (and pinned
+    // there): an LDS read that follows a pending LDS-bound load in program
+    // order gets a full vmcnt(0) wait from the compiler, which would
+    // serialise the ring.  Issued here they still have a whole stage to land.
     auto step = [&](const float* __restrict__ rd, float* __restrict__ wr, int s) __attribute__((always_inline)) {
-      issue(wr, s + 2);
       if (active) {
         auto fragA = [&](int i, int g) __attribute__((always_inline)) {
           const int row = wm + 32 * i + (lane & 31), quad = 2 * g + (lane >> 5);
@@ -552,6 +558,8 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
                   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(wr, s + 2);
       __builtin_amdgcn_s_waitcnt(kWaitAhead);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_s_barrier();
