@@ -427,9 +427,10 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
 // workgroup per CU.  Each thread moves one 16-byte piece of A and one of B
 // per k-stage straight into LDS (global_load_lds_dwordx4: lane l of a wave
 // writes 16 bytes at the wave's LDS base + 16 l), through a ring of three
-// stages: the loads for stage s + 2 leave at the end of stage s, and a stage
-// ends with a wait for the next stage's loads only, then one barrier.  Twice the tile
-// edge halves the operand traffic per flop of the 128 x 128 kernel.
+// stages: the loads for stage s + 2 leave at the start of stage s, and a
+// stage ends with a wait for the next stage's loads only, then one barrier.
+// Twice the tile edge halves the operand traffic per flop of the 128 x 128
+// kernel.
 //
 // LDS layout of a stage: A as [row][4 quads of 4 k], the quad index XOR-ed
 // with (row >> 1) & 3 so that the 16-byte fragment reads of 8 consecutive
@@ -516,12 +517,14 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
 
   auto mainloop = [&](auto skip) __attribute__((always_inline)) {
     constexpr bool kSkip = decltype(skip)::value;
-    // One stage: MFMAs on `rd` (stage s), then the loads for stage s + 2 into
-    // `wr`.  The loads are issued after this stage's LDS reads (and pinned
-    // there): an LDS read that follows a pending LDS-bound load in program
-    // order gets a full vmcnt(0) wait from the compiler, which would
-    // serialise the ring.  Issued here they still have a whole stage to land.
+    // One stage: the loads for stage s + 2 into `wr` (pinned at the head of
+    // the stage), then the MFMAs on `rd` (stage s).  The compiler lets the
+    // LDS reads of `rd` pass the pending loads only because it can tell the
+    // ring's buffers apart (restrict pointers into the kernel's one LDS
+    // array); otherwise it would wait for every load before each read.
     auto step = [&](const float* __restrict__ rd, float* __restrict__ wr, int s) __attribute__((always_inline)) {
+      issue(wr, s + 2);
+      __builtin_amdgcn_sched_barrier(0);
       if (active) {
         auto fragA = [&](int i, int g) __attribute__((always_inline)) {
           const int row = wm + 32 * i + (lane & 31), quad = 2 * g + (lane >> 5);
@@ -558,8 +561,6 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
                   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      issue(wr, s + 2);
       __builtin_amdgcn_s_waitcnt(kWaitAhead);
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_s_barrier();
