@@ -214,13 +214,15 @@ __device__ __forceinline__ float sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN
 // group of four accumulators a lane holds rows r..r+3 of one column c: it
 // writes them there (on a diagonal tile only on and above the diagonal) and
 // writes the mirrored entries, columns r..r+3 of row c, with one vector
-// store (on a diagonal tile only those strictly below the diagonal).
+// store (on a diagonal tile only those strictly below the diagonal).  Only
+// the 32 x 32 blocks (i, j) with bit i TN + j of `mask` set are written.
 template <int TM, int TN, class Tile>
 __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[TM][TN], int m0, int n0, int wm,
-                                                    int wn, int lane, bool diag) {
+                                                    int wn, int lane, bool diag, int mask) {
   const int h = lane >> 5, cl = lane & 31;
   static_for<TM * TN * 4>([&](auto G) __attribute__((always_inline)) {
     constexpr int i = decltype(G)::value / (TN * 4), j = (decltype(G)::value / 4) % TN, q = decltype(G)::value % 4;
+    if (!((mask >> (i * TN + j)) & 1)) return;  // a 32 x 32 block this wave did not compute
     const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
     const int c = n0 + wn + 32 * j + cl;
     const floatx4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
@@ -270,16 +272,18 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch<Epi>& P, uint32_t l
 // row = 32 i + 8 (e / 4) + 4 (lane / 32) + e % 4, col = 32 j + lane % 32 of the
 // wave's (32 TM) x (32 TN) part, at (wm, wn) in the tile at (m0, n0).  `lds`
 // must hold (BM / PH) x (BN + 1) floats and be free; `red` NT / 64 floats.
+// `mask` (the blocks this wave computed) is honoured by the register-direct
+// symmetric epilogue; the other paths need every block computed.
 template <int TM, int TN, int BM, int BN, int NT, int PH, bool SYM, class Epi>
 __device__ __forceinline__ void gemm_epilogue(const GemmLaunch<Epi>& P, int job, int64_t item, int tm, int tn,
                                               floatx16 (&acc)[TM][TN], float* lds, float* red, int m0, int n0,
-                                              int wm, int wn, int lane) {
+                                              int wm, int wn, int lane, int mask = (1 << (TM * TN)) - 1) {
   typename Epi::Tile tile(P.e[job], item, P.B);
   float part = 0.f;
   bool done = false;
   if constexpr (Epi::kSym && SYM) {
     if constexpr (Epi::kDirect && !Epi::kReduce)
-      sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn);
+      sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn, mask);
     else
       part = sym_epilogue<TM, TN, BM, BN, NT, PH, Epi::kReduce>(tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
     done = true;
@@ -441,8 +445,9 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
 //
 // Waves are placed on the 4 x 4 grid of 64 x 64 blocks so that on a diagonal
 // tile of a symmetric product (6 blocks idle below the diagonal, 4 on it at
-// three quarters of the work) each SIMD (wave % 4, assuming the dispatcher
-// deals waves round-robin) carries at most 2.5 blocks of work instead of 3.75.
+// three quarters of the work) the waves of each SIMD (w, w + 4, w + 8, w + 12
+// share one, as HW_ID shows) carry 2 or 2.5 blocks of work instead of up to
+// 3.75; two 32 x 32 blocks handed to idle waves even that out to 2.25.
 // ---------------------------------------------------------------------------
 constexpr int kBigThreads = 1024;
 constexpr int kBigTile = 256;
@@ -472,10 +477,22 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int place = (int)((kBigPlace >> (4 * wave)) & 15);
+  // The wave's 64 x 64 block and which of its four 32 x 32 blocks (bit
+  // 2 i + j) it computes.  Off-diagonal tiles: all four.  On a diagonal tile
+  // of a symmetric product: none below the diagonal, all but (1, 0) on it;
+  // and waves 2 and 3 (blocks (0, 3) and (1, 2)) hand their block (1, 1) to
+  // waves 8 and 9, idle below the diagonal on the SIMDs with less work, so
+  // that each SIMD computes 9 of the tile's 36 upper 32 x 32 blocks.
+  const bool dtile = SYM && tm == tn;
+  const bool helper = dtile && (wave == 8 || wave == 9);
+  const int place = (int)((kBigPlace >> (4 * (helper ? wave - 6 : wave))) & 15);
   const int wm = (place >> 2) * 64, wn = (place & 3) * 64;
-  const bool active = !(SYM && tm == tn && wm > wn);
-  const bool skip_low = SYM && tm == tn && wm == wn;
+  int mask = 0xF;
+  if (dtile) {
+    mask = wm > wn ? 0 : (wm == wn ? 0xB : 0xF);
+    if (wave == 2 || wave == 3) mask = 0x7;
+    if (helper) mask = 0x8;
+  }
 
   // this thread's pieces: A row r, quad q (stored at quad q ^ swz); B row k, columns 4 nq..
   const float* srcA;
@@ -515,8 +532,8 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
   __builtin_amdgcn_s_waitcnt(kWaitAhead);
   __builtin_amdgcn_s_barrier();
 
-  auto mainloop = [&](auto skip) __attribute__((always_inline)) {
-    constexpr bool kSkip = decltype(skip)::value;
+  auto mainloop = [&](auto M) __attribute__((always_inline)) {
+    constexpr int kMask = decltype(M)::value;
     // One stage: the loads for stage s + 2 into `wr` (pinned at the head of
     // the stage), then the MFMAs on `rd` (stage s).  The compiler lets the
     // LDS reads of `rd` pass the pending loads only because it can tell the
@@ -525,7 +542,9 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
     auto step = [&](const float* __restrict__ rd, float* __restrict__ wr, int s) __attribute__((always_inline)) {
       issue(wr, s + 2);
       __builtin_amdgcn_sched_barrier(0);
-      if (active) {
+      if constexpr (kMask != 0) {
+        constexpr int kRows = ((kMask & 3) ? 1 : 0) | ((kMask & 12) ? 2 : 0);  // block rows i in use
+        constexpr int kCols = ((kMask & 5) ? 1 : 0) | ((kMask & 10) ? 2 : 0);  // block columns j in use
         auto fragA = [&](int i, int g) __attribute__((always_inline)) {
           const int row = wm + 32 * i + (lane & 31), quad = 2 * g + (lane >> 5);
           return *reinterpret_cast<const floatx4*>(rd + 4 * (row * 4 + (quad ^ ((row >> 1) & 3))));
@@ -539,17 +558,21 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
         };
         floatx4 fa[2][TM], fb[2][TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) fa[0][i] = fragA(i, 0);
+        for (int i = 0; i < TM; ++i)
+          if ((kRows >> i) & 1) fa[0][i] = fragA(i, 0);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[0][j] = fragB(j, 0);
+        for (int j = 0; j < TN; ++j)
+          if ((kCols >> j) & 1) fb[0][j] = fragB(j, 0);
 #pragma unroll
         for (int g = 0; g < BK / 8; ++g) {
           const int c = g & 1;
           if (g + 1 < BK / 8) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) fa[c ^ 1][i] = fragA(i, g + 1);
+            for (int i = 0; i < TM; ++i)
+              if ((kRows >> i) & 1) fa[c ^ 1][i] = fragA(i, g + 1);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) fb[c ^ 1][j] = fragB(j, g + 1);
+            for (int j = 0; j < TN; ++j)
+              if ((kCols >> j) & 1) fb[c ^ 1][j] = fragB(j, g + 1);
           }
 #pragma unroll
           for (int q = 0; q < 4; ++q)
@@ -557,7 +580,7 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
             for (int i = 0; i < TM; ++i)
 #pragma unroll
               for (int j = 0; j < TN; ++j)
-                if (!kSkip || i <= j)
+                if ((kMask >> (2 * i + j)) & 1)
                   acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[c][i][q], fb[c][j][q], acc[i][j], 0, 0, 0);
         }
       }
@@ -575,15 +598,22 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
     if (s < nstages) step(b0, b2, s);
     if (s + 1 < nstages) step(b1, b0, s + 1);
   };
-  if (SYM && skip_low)
-    mainloop(std::true_type{});
-  else
-    mainloop(std::false_type{});
+  if constexpr (SYM) {
+    switch (mask) {
+      case 0xF: mainloop(std::integral_constant<int, 0xF>{}); break;
+      case 0xB: mainloop(std::integral_constant<int, 0xB>{}); break;
+      case 0x7: mainloop(std::integral_constant<int, 0x7>{}); break;
+      case 0x8: mainloop(std::integral_constant<int, 0x8>{}); break;
+      default: mainloop(std::integral_constant<int, 0>{}); break;
+    }
+  } else {
+    mainloop(std::integral_constant<int, 0xF>{});
+  }
   // drain the loads issued past the last stage before the epilogue reuses LDS
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __syncthreads();
 
-  gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM>(P, job, item, tm, tn, acc, lds, red, m0, n0, wm, wn, lane);
+  gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM>(P, job, item, tm, tn, acc, lds, red, m0, n0, wm, wn, lane, mask);
 }
 
 // ---------------------------------------------------------------------------

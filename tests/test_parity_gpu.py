@@ -166,6 +166,41 @@ def test_newton_matches_oracle(B, variant, p, iters, full):
     report("newton", B=B, variant=variant, p=p, iters=iters, full=full, err=err)
 
 
+@pytest.mark.parametrize("B", [512, 768])
+@pytest.mark.parametrize("solver,variant,arg,full", [("newton", capi.NDB_Z, 6, False), ("newton", capi.NDB, 6, False),
+                                                     ("newton", capi.NDB_Z, 6, True), ("newton", capi.CN, 6, False),
+                                                     ("cheby", None, 16, False)])
+def test_fp32_products_span_tiles(B, solver, variant, arg, full):
+    """fp32 roots on several output tiles per factor: B = 512 runs the 256 x 256
+    direct-to-LDS kernel on 2 x 2 tiles (3 upper tiles, two of them diagonal),
+    B = 768 the 128 x 128 kernel on 6 x 6 tiles; symmetric and full products,
+    reductions and epilogues all cross tile boundaries."""
+    nf = 3
+    F = W.spd_factors(70 + B, nf, B, cond=1e3)
+    V0 = W.start_vectors(71, nf, B)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    if solver == "newton":
+        v = variant | (capi.FULL_PRODUCTS if full else 0)
+        X, R = gpu_roots(Fd, sc, st, "newton", iters=arg, p=4, variant=v, resid=True)
+        assert np.all(np.isfinite(host(R)))
+    else:
+        X, _ = gpu_roots(Fd, sc, st, "cheby", degree=arg, prec=capi.F32)
+    Xh = host(X)
+    err = 0.0
+    for i in range(nf):
+        o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
+        if solver == "newton":
+            ref = oracle_root(F[i], o, "newton", iters=arg, p=4, variant=variant)
+        else:
+            ref = oracle_root(F[i], o, "cheby", degree=arg)
+        err = max(err, O.relative_frobenius(Xh[i], ref))
+    assert err <= TOL_F32, err
+    if not full and variant != capi.CN:
+        assert all(np.array_equal(Xh[i], Xh[i].T) for i in range(nf))
+    report("fp32_span_tiles", B=B, solver=solver, variant=variant, arg=arg, full=full, err=err)
+
+
 def test_newton_db_residuals_match_oracle():
     nf, B, k = 3, 128, 5
     F = W.spd_factors(40, nf, B, cond=1e2)
