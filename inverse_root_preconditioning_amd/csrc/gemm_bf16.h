@@ -290,7 +290,7 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
       return false;
     }();
     if constexpr (kDirect)
-      sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn, (1 << (TM * TN)) - 1);
+      sym_epilogue_direct<TM, TN, 8>(tile, acc, m0, n0, wm, wn, lane, tm == tn, (1 << (TM * TN)) - 1);
     else
       part = staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, reinterpret_cast<float*>(lds), m0, n0, wm,
                                                           wn, lane, SYM, tm == tn);
@@ -300,7 +300,7 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
       static_assert(sizeof(lds) >= sizeof(float) * (BM / PH) * (BN + 1), "LDS too small for the transpose");
       {
         if constexpr (Epi::kDirect && !Epi::kReduce)
-          sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn, (1 << (TM * TN)) - 1);
+          sym_epilogue_direct<TM, TN, 8>(tile, acc, m0, n0, wm, wn, lane, tm == tn, (1 << (TM * TN)) - 1);
         else
           part = sym_epilogue<TM, TN, BM, BN, NT, PH, Epi::kReduce>(tile, acc, reinterpret_cast<float*>(lds), m0,
                                                                      n0, wm, wn, lane, tm == tn);

@@ -216,17 +216,16 @@ __device__ __forceinline__ float sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN
 // writes the mirrored entries, columns r..r+3 of row c, with one vector
 // store (on a diagonal tile only those strictly below the diagonal).  Only
 // the 32 x 32 blocks (i, j) with bit i TN + j of `mask` set are written.
-template <int TM, int TN, class Tile>
+// KPRE bounds how many groups' epilogue inputs are loaded ahead (registers).
+template <int TM, int TN, int KPRE, class Tile>
 __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[TM][TN], int m0, int n0, int wm,
                                                     int wn, int lane, bool diag, int mask) {
   const int h = lane >> 5, cl = lane & 31;
-  static_for<TM * TN * 4>([&](auto G) __attribute__((always_inline)) {
+  // Forms and writes group G (block i, j; accumulators 4 q .. 4 q + 3).
+  auto emit = [&](auto G, const auto& o) __attribute__((always_inline)) {
     constexpr int i = decltype(G)::value / (TN * 4), j = (decltype(G)::value / 4) % TN, q = decltype(G)::value % 4;
-    if (!((mask >> (i * TN + j)) & 1)) return;  // a 32 x 32 block this wave did not compute
     const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
     const int c = n0 + wn + 32 * j + cl;
-    const floatx4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-    const floatx4 o = tile.value4(r, c, v);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (!diag || r + e <= c) tile.write_upper(r + e, c, o[e]);
@@ -237,7 +236,54 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
       for (int e = 0; e < 4; ++e)
         if (r + e < c) tile.write(c, r + e, o[e]);
     }
-  });
+  };
+  auto rc = [&](auto G, int& r, int& c) __attribute__((always_inline)) {
+    constexpr int i = decltype(G)::value / (TN * 4), j = (decltype(G)::value / 4) % TN, q = decltype(G)::value % 4;
+    r = m0 + wm + 32 * i + 8 * q + 4 * h;
+    c = n0 + wn + 32 * j + cl;
+  };
+  auto acc4 = [&](auto G) __attribute__((always_inline)) {
+    constexpr int i = decltype(G)::value / (TN * 4), j = (decltype(G)::value / 4) % TN, q = decltype(G)::value % 4;
+    return floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+  };
+  auto computed = [&](auto G) __attribute__((always_inline)) {
+    constexpr int i = decltype(G)::value / (TN * 4), j = (decltype(G)::value / 4) % TN;
+    return ((mask >> (i * TN + j)) & 1) != 0;  // a block this wave computed
+  };
+  // groups prefetched together: at most the epilogue's wish, the caller's register budget and the groups there are
+  constexpr int K0 = Tile::kPrefetch < KPRE ? Tile::kPrefetch : KPRE;
+  constexpr int K = K0 < TM * TN * 4 ? K0 : TM * TN * 4;
+  if constexpr (K == 0) {
+    static_for<TM * TN * 4>([&](auto G) __attribute__((always_inline)) {
+      if (!computed(G)) return;
+      int r, c;
+      rc(G, r, c);
+      emit(G, tile.value4(r, c, acc4(G)));
+    });
+  } else {
+    // The epilogue's own inputs for K groups are requested before any of
+    // them is used (stores in between would otherwise keep each load behind
+    // the previous group's stores, one memory latency per group).
+    static_assert((TM * TN * 4) % K == 0, "whole chunks");
+    static_for<TM * TN * 4 / K>([&](auto C) __attribute__((always_inline)) {
+      typename Tile::Pre pre[K];
+      static_for<K>([&](auto G) __attribute__((always_inline)) {
+        constexpr int g = decltype(C)::value * K + decltype(G)::value;
+        if (!computed(std::integral_constant<int, g>{})) return;
+        int r, c;
+        rc(std::integral_constant<int, g>{}, r, c);
+        pre[decltype(G)::value] = tile.prefetch4(r, c);
+      });
+      static_for<K>([&](auto G) __attribute__((always_inline)) {
+        constexpr int g = decltype(C)::value * K + decltype(G)::value;
+        const std::integral_constant<int, g> gi{};
+        if (!computed(gi)) return;
+        int r, c;
+        rc(gi, r, c);
+        emit(gi, tile.value4p(r, c, acc4(gi), pre[decltype(G)::value]));
+      });
+    });
+  }
 }
 
 // Workgroup lid -> (job, item, tile row tm, tile column tn), item-major: the
@@ -283,7 +329,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmLaunch<Epi>& P, int job,
   bool done = false;
   if constexpr (Epi::kSym && SYM) {
     if constexpr (Epi::kDirect && !Epi::kReduce)
-      sym_epilogue_direct<TM, TN>(tile, acc, m0, n0, wm, wn, lane, tm == tn, mask);
+      sym_epilogue_direct<TM, TN, NT == kGemmThreads ? 4 : 2>(tile, acc, m0, n0, wm, wn, lane, tm == tn, mask);
     else
       part = sym_epilogue<TM, TN, BM, BN, NT, PH, Epi::kReduce>(tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
     done = true;
@@ -650,6 +696,7 @@ struct EpiStore {
     int fmt16;           // H16_BF16 or H16_F16
   };
   struct Tile {
+    static constexpr int kPrefetch = 0;
     float* out;
     const float* cin;
     uint16_t* o16;
@@ -851,6 +898,10 @@ struct EpiClenshaw {
     float pexp;
   };
   struct Tile {
+    static constexpr int kPrefetch = 8;  // groups whose b1, b2 are loaded ahead
+    struct Pre {
+      floatx4 x1, x2;
+    };
     float* out;
     uint16_t* obf;
     int fmt;
@@ -894,17 +945,21 @@ struct EpiClenshaw {
     }
     // b1 and b2 come from symmetric steps (mirrored writes), so they are read
     // at the transposed position: row c, columns r..r+3, one vector load each.
-    __device__ __forceinline__ floatx4 value4(int r, int c, const floatx4& v) const {
+    __device__ __forceinline__ Pre prefetch4(int r, int c) const {
       const int64_t idx = (int64_t)c * B + r;
-      const floatx4 x1 = ldg(reinterpret_cast<const floatx4*>(b1 + idx));
-      const floatx4 x2 = ldg(reinterpret_cast<const floatx4*>(b2 + idx));
+      return Pre{ldg(reinterpret_cast<const floatx4*>(b1 + idx)), ldg(reinterpret_cast<const floatx4*>(b2 + idx))};
+    }
+    __device__ __forceinline__ floatx4 value4p(int r, int c, const floatx4& v, const Pre& p) const {
       floatx4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool dg = (r + e == c);
-        o[e] = ident ? (dg ? 1.f : 0.f) : mult * ((dg ? cj : 0.f) + k1 * v[e] - k2 * x1[e] - x2[e]);
+        o[e] = ident ? (dg ? 1.f : 0.f) : mult * ((dg ? cj : 0.f) + k1 * v[e] - k2 * p.x1[e] - p.x2[e]);
       }
       return o;
+    }
+    __device__ __forceinline__ floatx4 value4(int r, int c, const floatx4& v) const {
+      return value4p(r, c, v, prefetch4(r, c));
     }
     __device__ __forceinline__ void write4t(int c, int r, const floatx4& o) {
       const int64_t idx = (int64_t)c * B + r;
