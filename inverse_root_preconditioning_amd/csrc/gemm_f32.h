@@ -261,26 +261,32 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
       emit(G, tile.value4(r, c, acc4(G)));
     });
   } else {
-    // The epilogue's own inputs for K groups are requested before any of
-    // them is used (stores in between would otherwise keep each load behind
-    // the previous group's stores, one memory latency per group).
-    static_assert((TM * TN * 4) % K == 0, "whole chunks");
-    static_for<TM * TN * 4 / K>([&](auto C) __attribute__((always_inline)) {
-      typename Tile::Pre pre[K];
+    // The epilogue's own inputs are requested a chunk of K groups at a time,
+    // one chunk ahead of the groups being formed and written (stores in
+    // between would otherwise keep each load behind the previous group's
+    // stores, one memory latency per group).
+    constexpr int NC = TM * TN * 4 / K;
+    static_assert(NC * K == TM * TN * 4, "whole chunks");
+    typename Tile::Pre pre[2][K];
+    auto fetch = [&](auto C) __attribute__((always_inline)) {
       static_for<K>([&](auto G) __attribute__((always_inline)) {
         constexpr int g = decltype(C)::value * K + decltype(G)::value;
         if (!computed(std::integral_constant<int, g>{})) return;
         int r, c;
         rc(std::integral_constant<int, g>{}, r, c);
-        pre[decltype(G)::value] = tile.prefetch4(r, c);
+        pre[decltype(C)::value & 1][decltype(G)::value] = tile.prefetch4(r, c);
       });
+    };
+    fetch(std::integral_constant<int, 0>{});
+    static_for<NC>([&](auto C) __attribute__((always_inline)) {
+      if constexpr (decltype(C)::value + 1 < NC) fetch(std::integral_constant<int, decltype(C)::value + 1>{});
       static_for<K>([&](auto G) __attribute__((always_inline)) {
         constexpr int g = decltype(C)::value * K + decltype(G)::value;
         const std::integral_constant<int, g> gi{};
         if (!computed(gi)) return;
         int r, c;
         rc(gi, r, c);
-        emit(gi, tile.value4p(r, c, acc4(gi), pre[decltype(G)::value]));
+        emit(gi, tile.value4p(r, c, acc4(gi), pre[decltype(C)::value & 1][decltype(G)::value]));
       });
     });
   }
@@ -329,7 +335,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmLaunch<Epi>& P, int job,
   bool done = false;
   if constexpr (Epi::kSym && SYM) {
     if constexpr (Epi::kDirect && !Epi::kReduce)
-      sym_epilogue_direct<TM, TN, NT == kGemmThreads ? 4 : 2>(tile, acc, m0, n0, wm, wn, lane, tm == tn, mask);
+      sym_epilogue_direct<TM, TN, NT == kGemmThreads ? 2 : 1>(tile, acc, m0, n0, wm, wn, lane, tm == tn, mask);
     else
       part = sym_epilogue<TM, TN, BM, BN, NT, PH, Epi::kReduce>(tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
     done = true;
@@ -898,7 +904,7 @@ struct EpiClenshaw {
     float pexp;
   };
   struct Tile {
-    static constexpr int kPrefetch = 8;  // groups whose b1, b2 are loaded ahead
+    static constexpr int kPrefetch = 4;  // groups whose b1, b2 are loaded per chunk
     struct Pre {
       floatx4 x1, x2;
     };
