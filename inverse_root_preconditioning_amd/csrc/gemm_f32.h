@@ -489,9 +489,10 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
 // kernel.
 //
 // LDS layout of a stage: A as [row][4 quads of 4 k], the quad index XOR-ed
-// with (row >> 1) & 3 so that the 16-byte fragment reads of 8 consecutive
-// rows hit 8 different bank groups; B as [k][256] (fragment reads run along
-// n, conflict free).  Every stage issues its loads, past the last stage again
+// with big_swz(row) so that the 16-byte fragment reads hit every bank once;
+// B as [k][256] with rows 4..7 of each group of 8 rotated by 32 columns, so
+// that a fragment read (lanes 0..31 along row k, lanes 32..63 along row
+// k + 4) covers all 64 banks.  Every stage issues its loads, past the last stage again
 // the last one into the free buffer, so the count of loads in flight, and
 // hence each wait, is the same on every path.
 //
@@ -503,6 +504,10 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
 // ---------------------------------------------------------------------------
 constexpr int kBigThreads = 1024;
 constexpr int kBigTile = 256;
+// XOR swizzle of the 16-byte k-quads of A's rows (4 per row): the fragment
+// reads of 16 consecutive rows then cover all 64 banks (256 bytes) of LDS,
+// and so do those of each 8 consecutive rows within 128 bytes.
+__device__ __forceinline__ int big_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 // block (row, col) of wave w: 4 bits r * 4 + c per wave, w = 0 in the low bits
 constexpr uint64_t kBigPlace = 0x9CDEF584A07B6321ull;
 
@@ -550,9 +555,9 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
   const float* srcA;
   const float* srcB;
   {
-    const int r = tid >> 2, qs = tid & 3, qg = qs ^ ((r >> 1) & 3);
+    const int r = tid >> 2, qs = tid & 3, qg = qs ^ big_swz(r);
     srcA = pa + (int64_t)(m0 + r) * B + 4 * qg;
-    const int k = tid >> 6, nq = tid & 63;
+    const int k = tid >> 6, nq = (tid & 63) ^ (((k >> 2) & 1) << 3);  // rows 4..7 of each 8 shifted by 128 B
     srcB = pb + (int64_t)k * B + n0 + 4 * nq;
   }
   const int nstages = B / BK;
@@ -599,10 +604,11 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
         constexpr int kCols = ((kMask & 5) ? 1 : 0) | ((kMask & 10) ? 2 : 0);  // block columns j in use
         auto fragA = [&](int i, int g) __attribute__((always_inline)) {
           const int row = wm + 32 * i + (lane & 31), quad = 2 * g + (lane >> 5);
-          return *reinterpret_cast<const floatx4*>(rd + 4 * (row * 4 + (quad ^ ((row >> 1) & 3))));
+          return *reinterpret_cast<const floatx4*>(rd + 4 * (row * 4 + (quad ^ big_swz(row))));
         };
         auto fragB = [&](int j, int g) __attribute__((always_inline)) {
-          const float* q = rd + kA + (g * 8 + (lane >> 5) * 4) * BN + wn + 32 * j + (lane & 31);
+          // lanes 32..63 read rows 4..7 of the group, stored 32 columns over
+          const float* q = rd + kA + (g * 8 + (lane >> 5) * 4) * BN + ((wn + 32 * j + (lane & 31)) ^ ((lane >> 5) << 5));
           floatx4 x;
 #pragma unroll
           for (int e = 0; e < 4; ++e) x[e] = q[e * BN];
