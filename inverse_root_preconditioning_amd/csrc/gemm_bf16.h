@@ -20,6 +20,8 @@ constexpr int kLd16 = kBK16 + 8;  // LDS row stride in bf16 elements (144 bytes)
 struct EpiStoreBf16 {
   static constexpr bool kSym = false;
   static constexpr bool kReduce = false;
+  static constexpr bool kBigSym = false, kBigFull = true;
+  static constexpr bool kH16BigSym = false, kH16BigFull = true;
   struct Job {
     uint16_t* out;
   };
@@ -37,6 +39,7 @@ struct EpiStoreBf16 {
 
 template <class Epi>
 struct H16Launch {
+  using EpiT = Epi;
   const uint16_t* a[2];
   const uint16_t* bt[2];
   typename Epi::Job e[2];
@@ -419,12 +422,161 @@ static inline int bf16_gather(const shampoo_block* d, int64_t n, int B, uint16_t
 }
 
 // One launch of up to two NT products of 16-bit stacks with the same epilogue type.
+// ---------------------------------------------------------------------------
+// 16-bit products on 256 x 256 tiles (B a multiple of 256, epilogues that fit
+// 128 VGPRs): 16 waves of 64 x 64 (2 x 2 blocks of the 32 x 32 x 16 MFMA),
+// one workgroup per CU.  Each thread moves two 16-byte pieces of A and two of
+// Bt per 64-deep k stage straight into LDS (global_load_lds_dwordx4) into the
+// other of two stage buffers while the MFMAs run on the current one; a stage
+// ends with a wait for its loads and one barrier.  Rows are stored as 8
+// chunks of 16 bytes with the chunk index XOR-ed by (row ^ (row >> 3)) & 7,
+// so the fragment reads of 16 consecutive rows cover all 64 banks.  Waves are
+// placed, and their blocks on diagonal tiles of symmetric products assigned,
+// as in gemm_f32_big_kernel.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int h16_swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+template <class Epi, int FMT, bool SYM>
+__global__ void __launch_bounds__(kBigThreads, 1) gemm_h16_big_kernel(const H16Launch<Epi> P) {
+  constexpr int TM = 2, TN = 2, BM = kBigTile, BN = kBigTile, BKS = 64, NT = kBigThreads;
+  constexpr int CPR = BKS / 8;                           // 16-byte chunks per staged row
+  constexpr int kA = BM * BKS, kStage = (BM + BN) * BKS;  // 16-bit elements
+  constexpr int LA = BM * CPR / NT;                      // chunks of A (and of Bt) per thread and stage
+  constexpr int KS = BKS / 16;
+  constexpr int PH = 4;                                  // phases of the symmetric epilogue's transpose
+  constexpr int kFloats = 2 * kStage / 2;                // the stage buffers, counted in floats
+  static_assert(LA * NT == BM * CPR && BN == BM, "chunking");
+  static_assert((BM / PH) * (BN + 1) + NT / kWave <= kFloats, "transpose and reduction fit the buffers");
+  // One LDS object only (see gemm_f32_big_kernel).
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+  float* const red = reinterpret_cast<float*>(lds) + kFloats - NT / kWave;
+
+  int job, tm, tn;
+  int64_t item;
+  decode_tile<SYM>(P, xcd_remap(blockIdx.x, P.total), job, item, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int B = P.B;
+  const int64_t off = item * (int64_t)B * B;
+  const uint16_t* A = (job == 0 ? P.a[0] : P.a[1]) + off;
+  const uint16_t* Bt = (job == 0 ? P.bt[0] : P.bt[1]) + off;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int wm, wn, mask;
+  big_wave_role(SYM && tm == tn, wave, wm, wn, mask);
+  const int rr = lane & 31, h = lane >> 5;
+
+  const uint16_t* srcA[LA];
+  const uint16_t* srcB[LA];
+#pragma unroll
+  for (int it = 0; it < LA; ++it) {
+    const int c = it * NT + tid, row = c / CPR, cs = (c % CPR) ^ h16_swz(c / CPR);
+    srcA[it] = A + (int64_t)(m0 + row) * B + 8 * cs;
+    srcB[it] = Bt + (int64_t)(n0 + row) * B + 8 * cs;
+  }
+  const int nstages = B / BKS;
+  auto issue = [&](uint16_t* __restrict__ buf, int s) __attribute__((always_inline)) {
+    const int k0 = min(s, nstages - 1) * BKS;
+#pragma unroll
+    for (int it = 0; it < LA; ++it) {
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcA[it] + k0),
+                                       (__attribute__((address_space(3))) void*)(buf + (it * NT + wave * 64) * 8),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcB[it] + k0),
+                                       (__attribute__((address_space(3))) void*)(buf + kA + (it * NT + wave * 64) * 8),
+                                       16, 0, 0);
+    }
+  };
+  constexpr int kWaitAll = 0 | (7 << 4);  // vmcnt(0) lgkmcnt(0)
+
+  floatx16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  uint16_t* const b0 = lds;
+  uint16_t* const b1 = lds + kStage;
+  issue(b0, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
+  __builtin_amdgcn_s_barrier();
+
+  auto mainloop = [&](auto M) __attribute__((always_inline)) {
+    constexpr int kMask = decltype(M)::value;
+    // One stage: the loads for stage s + 1 into `wr` (read at stage s - 1,
+    // free since that stage's barrier), then the MFMAs on `rd`.
+    auto step = [&](const uint16_t* __restrict__ rd, uint16_t* __restrict__ wr, int s) __attribute__((always_inline)) {
+      issue(wr, s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kMask != 0) {
+        constexpr int kRows = ((kMask & 3) ? 1 : 0) | ((kMask & 12) ? 2 : 0);
+        constexpr int kCols = ((kMask & 5) ? 1 : 0) | ((kMask & 10) ? 2 : 0);
+        auto frag = [&](const uint16_t* base, int row, int ks) __attribute__((always_inline)) {
+          return *reinterpret_cast<const u32x4*>(base + (row * CPR + ((2 * ks + h) ^ h16_swz(row))) * 8);
+        };
+        u32x4 ca[2][TM], cb[2][TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          if ((kRows >> i) & 1) ca[0][i] = frag(rd, wm + 32 * i + rr, 0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          if ((kCols >> j) & 1) cb[0][j] = frag(rd + kA, wn + 32 * j + rr, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int c = ks & 1;
+          if (ks + 1 < KS) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+              if ((kRows >> i) & 1) ca[c ^ 1][i] = frag(rd, wm + 32 * i + rr, ks + 1);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              if ((kCols >> j) & 1) cb[c ^ 1][j] = frag(rd + kA, wn + 32 * j + rr, ks + 1);
+          }
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              if ((kMask >> (2 * i + j)) & 1) acc[i][j] = mfma_h16<FMT>(ca[c][i], cb[c][j], acc[i][j]);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    int s = 0;
+    for (; s + 2 <= nstages; s += 2) {
+      step(b0, b1, s);
+      step(b1, b0, s + 1);
+    }
+    if (s < nstages) step(b0, b1, s);
+  };
+  if constexpr (SYM) {
+    switch (mask) {
+      case 0xF: mainloop(std::integral_constant<int, 0xF>{}); break;
+      case 0xB: mainloop(std::integral_constant<int, 0xB>{}); break;
+      case 0x7: mainloop(std::integral_constant<int, 0x7>{}); break;
+      case 0x8: mainloop(std::integral_constant<int, 0x8>{}); break;
+      default: mainloop(std::integral_constant<int, 0>{}); break;
+    }
+  } else {
+    mainloop(std::integral_constant<int, 0xF>{});
+  }
+  __syncthreads();  // every load has landed (each stage ended with vmcnt(0)); the epilogue may reuse LDS
+
+  gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM>(P, job, item, tm, tn, acc, reinterpret_cast<float*>(lds), red, m0, n0,
+                                             wm, wn, lane, mask);
+}
+
 template <class Epi>
 static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* bt, const typename Epi::Job* e,
                               int njobs, int64_t n, int B, bool sym, int fmt, hipStream_t st) {
   if (B % 128 != 0) return SHAMPOO_EUNSUPPORTED;
   if (!Epi::kSym && sym) return SHAMPOO_EINVAL;  // no symmetric epilogue
-  const int T = h16_tile_of(B, sym);
+  const bool big = B % kBigTile == 0 && (sym ? Epi::kH16BigSym : Epi::kH16BigFull);
+  const int T = big ? kBigTile : h16_tile_of(B, sym);
   H16Launch<Epi> P;
   memset(&P, 0, sizeof(P));
   for (int j = 0; j < njobs; ++j) {
@@ -440,6 +592,29 @@ static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* b
   if (total == 0) return SHAMPOO_OK;
   if (total > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
   P.total = (uint32_t)total;
+  if (big) {
+    bool launched = false;
+    if constexpr (Epi::kSym && Epi::kH16BigSym) {
+      if (sym) {
+        if (fmt == H16_F16)
+          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_F16, true>), dim3(P.total), dim3(kBigThreads), 0, st, P);
+        else
+          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_BF16, true>), dim3(P.total), dim3(kBigThreads), 0, st, P);
+        launched = true;
+      }
+    }
+    if constexpr (Epi::kH16BigFull) {
+      if (!sym) {
+        if (fmt == H16_F16)
+          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_F16, false>), dim3(P.total), dim3(kBigThreads), 0, st, P);
+        else
+          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_BF16, false>), dim3(P.total), dim3(kBigThreads), 0, st, P);
+        launched = true;
+      }
+    }
+    if (!launched) return SHAMPOO_EUNSUPPORTED;  // unreachable: `big` chose this kernel
+    return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMPOO_EHIP;
+  }
   if (T == 256) {
     constexpr int NT = H16Shape<H16_T256>::NT;
     if constexpr (Epi::kSym) {

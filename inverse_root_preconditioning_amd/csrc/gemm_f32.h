@@ -135,6 +135,7 @@ struct Stager {
 // Launch parameters; Epi::Job carries the epilogue's per-job arguments.
 template <class Epi>
 struct GemmLaunch {
+  using EpiT = Epi;
   Operand a[2];
   Operand b[2];
   typename Epi::Job e[2];
@@ -296,8 +297,8 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
 // tiles of both jobs of one item are neighbours, so that the workgroups that
 // run together share that item's operands (E in Y E and E Z) through L2.  A
 // symmetric product enumerates only its upper tiles (tm <= tn), row by row.
-template <bool SYM, class Epi>
-__device__ __forceinline__ void decode_tile(const GemmLaunch<Epi>& P, uint32_t lid, int& job, int64_t& item, int& tm,
+template <bool SYM, class L>
+__device__ __forceinline__ void decode_tile(const L& P, uint32_t lid, int& job, int64_t& item, int& tm,
                                             int& tn) {
   const uint32_t tpi = (uint32_t)P.tiles_per_item;
   const uint32_t njobs = P.total / ((uint32_t)P.nitems * tpi);
@@ -326,11 +327,12 @@ __device__ __forceinline__ void decode_tile(const GemmLaunch<Epi>& P, uint32_t l
 // must hold (BM / PH) x (BN + 1) floats and be free; `red` NT / 64 floats.
 // `mask` (the blocks this wave computed) is honoured by the register-direct
 // symmetric epilogue; the other paths need every block computed.
-template <int TM, int TN, int BM, int BN, int NT, int PH, bool SYM, class Epi>
-__device__ __forceinline__ void gemm_epilogue(const GemmLaunch<Epi>& P, int job, int64_t item, int tm, int tn,
+template <int TM, int TN, int BM, int BN, int NT, int PH, bool SYM, class L>
+__device__ __forceinline__ void gemm_epilogue(const L& P, int job, int64_t item, int tm, int tn,
                                               floatx16 (&acc)[TM][TN], float* lds, float* red, int m0, int n0,
                                               int wm, int wn, int lane, int mask = (1 << (TM * TN)) - 1) {
-  typename Epi::Tile tile(P.e[job], item, P.B);
+  using Epi = typename L::EpiT;
+  typename Epi::Tile tile(*(job == 0 ? &P.e[0] : &P.e[1]), item, P.B);
   float part = 0.f;
   bool done = false;
   if constexpr (Epi::kSym && SYM) {
@@ -504,12 +506,32 @@ __global__ void __launch_bounds__(kGemmThreads, MINW) gemm_f32_kernel(const Gemm
 // ---------------------------------------------------------------------------
 constexpr int kBigThreads = 1024;
 constexpr int kBigTile = 256;
+// block (row, col) of wave w: 4 bits r * 4 + c per wave, w = 0 in the low bits
+constexpr uint64_t kBigPlace = 0x9CDEF584A07B6321ull;
 // XOR swizzle of the 16-byte k-quads of A's rows (4 per row): the fragment
 // reads of 16 consecutive rows then cover all 64 banks (256 bytes) of LDS,
 // and so do those of each 8 consecutive rows within 128 bytes.
 __device__ __forceinline__ int big_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
-// block (row, col) of wave w: 4 bits r * 4 + c per wave, w = 0 in the low bits
-constexpr uint64_t kBigPlace = 0x9CDEF584A07B6321ull;
+
+// The 64 x 64 block (wm, wn) of wave `wave` of a 256 x 256 tile and which of
+// its four 32 x 32 blocks (bit 2 i + j) it computes.  Off-diagonal tiles:
+// all four.  On a diagonal tile of a symmetric product: none below the
+// diagonal, all but (1, 0) on it; and waves 2 and 3 (blocks (0, 3) and
+// (1, 2)) hand their block (1, 1) to waves 8 and 9, idle below the diagonal
+// on the SIMDs with less work, so that each SIMD computes 9 of the tile's 36
+// upper 32 x 32 blocks.
+__device__ __forceinline__ void big_wave_role(bool dtile, int wave, int& wm, int& wn, int& mask) {
+  const bool helper = dtile && (wave == 8 || wave == 9);
+  const int place = (int)((kBigPlace >> (4 * (helper ? wave - 6 : wave))) & 15);
+  wm = (place >> 2) * 64;
+  wn = (place & 3) * 64;
+  mask = 0xF;
+  if (dtile) {
+    mask = wm > wn ? 0 : (wm == wn ? 0xB : 0xF);
+    if (wave == 2 || wave == 3) mask = 0x7;
+    if (helper) mask = 0x8;
+  }
+}
 
 template <class Epi, bool SYM>
 __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const GemmLaunch<Epi> P) {
@@ -534,22 +556,8 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // The wave's 64 x 64 block and which of its four 32 x 32 blocks (bit
-  // 2 i + j) it computes.  Off-diagonal tiles: all four.  On a diagonal tile
-  // of a symmetric product: none below the diagonal, all but (1, 0) on it;
-  // and waves 2 and 3 (blocks (0, 3) and (1, 2)) hand their block (1, 1) to
-  // waves 8 and 9, idle below the diagonal on the SIMDs with less work, so
-  // that each SIMD computes 9 of the tile's 36 upper 32 x 32 blocks.
-  const bool dtile = SYM && tm == tn;
-  const bool helper = dtile && (wave == 8 || wave == 9);
-  const int place = (int)((kBigPlace >> (4 * (helper ? wave - 6 : wave))) & 15);
-  const int wm = (place >> 2) * 64, wn = (place & 3) * 64;
-  int mask = 0xF;
-  if (dtile) {
-    mask = wm > wn ? 0 : (wm == wn ? 0xB : 0xF);
-    if (wave == 2 || wave == 3) mask = 0x7;
-    if (helper) mask = 0x8;
-  }
+  int wm, wn, mask;
+  big_wave_role(SYM && tm == tn, wave, wm, wn, mask);
 
   // this thread's pieces: A row r, quad q (stored at quad q ^ swz); B row k, columns 4 nq..
   const float* srcA;
@@ -695,8 +703,10 @@ struct EpiStore {
   static constexpr bool kReduce = false;
   static constexpr bool kSym = true;
   static constexpr bool kDirect = true;
-  // gemm_f32_big_kernel fits 128 VGPRs without spilling (symmetric / full)
+  // gemm_f32_big_kernel fits 128 VGPRs without spilling (symmetric / full);
+  // kH16Big*: the same for gemm_h16_big_kernel, where it also has to pay off
   static constexpr bool kBigSym = true, kBigFull = false;
+  static constexpr bool kH16BigSym = true, kH16BigFull = false;
   struct Job {
     float* out;          // fp32 output (may be null when only the 16-bit copy is needed)
     const float* cin;
@@ -765,6 +775,7 @@ struct EpiPair : EpiStore {};
 // Output through a block descriptor: only rows x cols of the block is written.
 struct EpiStoreDesc {
   static constexpr bool kBigSym = false, kBigFull = true;
+  static constexpr bool kH16BigSym = false, kH16BigFull = true;
   static constexpr bool kSym = false;
   static constexpr bool kReduce = false;
   struct Job {
@@ -798,6 +809,7 @@ struct EpiNdbE {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = false;
   static constexpr bool kBigSym = false, kBigFull = true;
+  static constexpr bool kH16BigSym = false, kH16BigFull = false;
   static constexpr bool kReduce = true;
   struct Job {
     float* e;
@@ -835,6 +847,7 @@ struct EpiCnM {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = false;
   static constexpr bool kBigSym = false, kBigFull = false;
+  static constexpr bool kH16BigSym = false, kH16BigFull = false;
   static constexpr bool kReduce = true;
   struct Job {
     float* m;            // fp32 outputs (null: not written)
@@ -897,6 +910,9 @@ struct EpiClenshaw {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = true;
   static constexpr bool kBigSym = true, kBigFull = false;
+  // 16-bit: the 8-wave 256 x 256 kernel, whose epilogue can load 4 groups of
+  // b1/b2 ahead (measured faster than the 16-wave kernel for this product)
+  static constexpr bool kH16BigSym = false, kH16BigFull = false;
   struct Job {
     float* out;
     uint16_t* out16;     // optional 16-bit copy of b (operand of the next product)
