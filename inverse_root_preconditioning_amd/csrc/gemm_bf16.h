@@ -22,6 +22,7 @@ struct EpiStoreBf16 {
   static constexpr bool kReduce = false;
   static constexpr bool kBigSym = false, kBigFull = true;
   static constexpr bool kH16BigSym = false, kH16BigFull = true;
+  static constexpr int kH16BigWaves = 16;
   struct Job {
     uint16_t* out;
   };
@@ -436,9 +437,15 @@ static inline int bf16_gather(const shampoo_block* d, int64_t n, int B, uint16_t
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int h16_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-template <class Epi, int FMT, bool SYM>
-__global__ void __launch_bounds__(kBigThreads, 1) gemm_h16_big_kernel(const H16Launch<Epi> P) {
-  constexpr int TM = 2, TN = 2, BM = kBigTile, BN = kBigTile, BKS = 64, NT = kBigThreads;
+// WAVES = 16: 4 x 4 waves of 64 x 64 (128 VGPRs each).  WAVES = 8: 4 x 2 waves
+// of 64 x 128 (256 VGPRs each), for epilogues that want registers to load
+// ahead; on a diagonal tile of a symmetric product its waves wholly below
+// the diagonal idle and the others compute their whole block.
+template <class Epi, int FMT, bool SYM, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16Launch<Epi> P) {
+  static_assert(WAVES == 16 || WAVES == 8, "wave layouts");
+  constexpr int TM = 2, TN = WAVES == 16 ? 2 : 4, BM = kBigTile, BN = kBigTile, BKS = 64, NT = 64 * WAVES;
+  constexpr int kFull = (1 << (TM * TN)) - 1;
   constexpr int CPR = BKS / 8;                           // 16-byte chunks per staged row
   constexpr int kA = BM * BKS, kStage = (BM + BN) * BKS;  // 16-bit elements
   constexpr int LA = BM * CPR / NT;                      // chunks of A (and of Bt) per thread and stage
@@ -463,7 +470,13 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_h16_big_kernel(const H16L
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int wm, wn, mask;
-  big_wave_role(SYM && tm == tn, wave, wm, wn, mask);
+  if constexpr (WAVES == 16) {
+    big_wave_role(SYM && tm == tn, wave, wm, wn, mask);
+  } else {
+    wm = (wave >> 1) * 64;
+    wn = (wave & 1) * 128;
+    mask = (SYM && tm == tn && wm >= wn + 128) ? 0 : kFull;
+  }
   const int rr = lane & 31, h = lane >> 5;
 
   const uint16_t* srcA[LA];
@@ -511,8 +524,18 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_h16_big_kernel(const H16L
       issue(wr, s + 1);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kMask != 0) {
-        constexpr int kRows = ((kMask & 3) ? 1 : 0) | ((kMask & 12) ? 2 : 0);
-        constexpr int kCols = ((kMask & 5) ? 1 : 0) | ((kMask & 10) ? 2 : 0);
+        // block rows i and columns j that any computed block uses
+        constexpr int kRows = [] {
+          int r = 0;
+          for (int i = 0; i < TM; ++i)
+            if ((kMask >> (i * TN)) & ((1 << TN) - 1)) r |= 1 << i;
+          return r;
+        }();
+        constexpr int kCols = [] {
+          int c = 0;
+          for (int i = 0; i < TM; ++i) c |= (kMask >> (i * TN)) & ((1 << TN) - 1);
+          return c;
+        }();
         auto frag = [&](const uint16_t* base, int row, int ks) __attribute__((always_inline)) {
           return *reinterpret_cast<const u32x4*>(base + (row * CPR + ((2 * ks + h) ^ h16_swz(row))) * 8);
         };
@@ -538,7 +561,7 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_h16_big_kernel(const H16L
           for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              if ((kMask >> (2 * i + j)) & 1) acc[i][j] = mfma_h16<FMT>(ca[c][i], cb[c][j], acc[i][j]);
+              if ((kMask >> (i * TN + j)) & 1) acc[i][j] = mfma_h16<FMT>(ca[c][i], cb[c][j], acc[i][j]);
         }
       }
       __builtin_amdgcn_s_waitcnt(kWaitAll);
@@ -553,7 +576,7 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_h16_big_kernel(const H16L
     }
     if (s < nstages) step(b0, b1, s);
   };
-  if constexpr (SYM) {
+  if constexpr (SYM && WAVES == 16) {
     switch (mask) {
       case 0xF: mainloop(std::integral_constant<int, 0xF>{}); break;
       case 0xB: mainloop(std::integral_constant<int, 0xB>{}); break;
@@ -561,13 +584,19 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_h16_big_kernel(const H16L
       case 0x8: mainloop(std::integral_constant<int, 0x8>{}); break;
       default: mainloop(std::integral_constant<int, 0>{}); break;
     }
+  } else if constexpr (SYM) {
+    if (mask)
+      mainloop(std::integral_constant<int, kFull>{});
+    else
+      mainloop(std::integral_constant<int, 0>{});
   } else {
-    mainloop(std::integral_constant<int, 0xF>{});
+    mainloop(std::integral_constant<int, kFull>{});
   }
   __syncthreads();  // every load has landed (each stage ended with vmcnt(0)); the epilogue may reuse LDS
 
-  gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM>(P, job, item, tm, tn, acc, reinterpret_cast<float*>(lds), red, m0, n0,
-                                             wm, wn, lane, mask);
+  gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM, WAVES == 16 ? 1 : 8>(P, job, item, tm, tn, acc,
+                                                                   reinterpret_cast<float*>(lds), red, m0, n0, wm,
+                                                                   wn, lane, mask);
 }
 
 template <class Epi>
@@ -594,21 +623,22 @@ static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* b
   P.total = (uint32_t)total;
   if (big) {
     bool launched = false;
+    constexpr int W = Epi::kH16BigWaves;
     if constexpr (Epi::kSym && Epi::kH16BigSym) {
       if (sym) {
         if (fmt == H16_F16)
-          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_F16, true>), dim3(P.total), dim3(kBigThreads), 0, st, P);
+          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_F16, true, W>), dim3(P.total), dim3(64 * W), 0, st, P);
         else
-          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_BF16, true>), dim3(P.total), dim3(kBigThreads), 0, st, P);
+          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_BF16, true, W>), dim3(P.total), dim3(64 * W), 0, st, P);
         launched = true;
       }
     }
     if constexpr (Epi::kH16BigFull) {
       if (!sym) {
         if (fmt == H16_F16)
-          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_F16, false>), dim3(P.total), dim3(kBigThreads), 0, st, P);
+          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_F16, false, W>), dim3(P.total), dim3(64 * W), 0, st, P);
         else
-          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_BF16, false>), dim3(P.total), dim3(kBigThreads), 0, st, P);
+          hipLaunchKernelGGL((gemm_h16_big_kernel<Epi, H16_BF16, false, W>), dim3(P.total), dim3(64 * W), 0, st, P);
         launched = true;
       }
     }

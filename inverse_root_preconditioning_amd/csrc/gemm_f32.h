@@ -327,7 +327,7 @@ __device__ __forceinline__ void decode_tile(const L& P, uint32_t lid, int& job, 
 // must hold (BM / PH) x (BN + 1) floats and be free; `red` NT / 64 floats.
 // `mask` (the blocks this wave computed) is honoured by the register-direct
 // symmetric epilogue; the other paths need every block computed.
-template <int TM, int TN, int BM, int BN, int NT, int PH, bool SYM, class L>
+template <int TM, int TN, int BM, int BN, int NT, int PH, bool SYM, int KPRE = (NT == kGemmThreads ? 2 : 1), class L>
 __device__ __forceinline__ void gemm_epilogue(const L& P, int job, int64_t item, int tm, int tn,
                                               floatx16 (&acc)[TM][TN], float* lds, float* red, int m0, int n0,
                                               int wm, int wn, int lane, int mask = (1 << (TM * TN)) - 1) {
@@ -337,7 +337,7 @@ __device__ __forceinline__ void gemm_epilogue(const L& P, int job, int64_t item,
   bool done = false;
   if constexpr (Epi::kSym && SYM) {
     if constexpr (Epi::kDirect && !Epi::kReduce)
-      sym_epilogue_direct<TM, TN, NT == kGemmThreads ? 2 : 1>(tile, acc, m0, n0, wm, wn, lane, tm == tn, mask);
+      sym_epilogue_direct<TM, TN, KPRE>(tile, acc, m0, n0, wm, wn, lane, tm == tn, mask);
     else
       part = sym_epilogue<TM, TN, BM, BN, NT, PH, Epi::kReduce>(tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
     done = true;
@@ -707,6 +707,7 @@ struct EpiStore {
   // kH16Big*: the same for gemm_h16_big_kernel, where it also has to pay off
   static constexpr bool kBigSym = true, kBigFull = false;
   static constexpr bool kH16BigSym = true, kH16BigFull = false;
+  static constexpr int kH16BigWaves = 16;
   struct Job {
     float* out;          // fp32 output (may be null when only the 16-bit copy is needed)
     const float* cin;
@@ -776,6 +777,7 @@ struct EpiPair : EpiStore {};
 struct EpiStoreDesc {
   static constexpr bool kBigSym = false, kBigFull = true;
   static constexpr bool kH16BigSym = false, kH16BigFull = true;
+  static constexpr int kH16BigWaves = 16;
   static constexpr bool kSym = false;
   static constexpr bool kReduce = false;
   struct Job {
@@ -810,6 +812,7 @@ struct EpiNdbE {
   static constexpr bool kDirect = false;
   static constexpr bool kBigSym = false, kBigFull = true;
   static constexpr bool kH16BigSym = false, kH16BigFull = false;
+  static constexpr int kH16BigWaves = 16;
   static constexpr bool kReduce = true;
   struct Job {
     float* e;
@@ -848,6 +851,7 @@ struct EpiCnM {
   static constexpr bool kDirect = false;
   static constexpr bool kBigSym = false, kBigFull = false;
   static constexpr bool kH16BigSym = false, kH16BigFull = false;
+  static constexpr int kH16BigWaves = 16;
   static constexpr bool kReduce = true;
   struct Job {
     float* m;            // fp32 outputs (null: not written)
@@ -910,9 +914,10 @@ struct EpiClenshaw {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = true;
   static constexpr bool kBigSym = true, kBigFull = false;
-  // 16-bit: the 8-wave 256 x 256 kernel, whose epilogue can load 4 groups of
-  // b1/b2 ahead (measured faster than the 16-wave kernel for this product)
-  static constexpr bool kH16BigSym = false, kH16BigFull = false;
+  // 16-bit: the 8-wave layout, whose registers let the epilogue load 4
+  // groups of b1/b2 ahead (the 16-wave one, with 1, measured slower)
+  static constexpr bool kH16BigSym = true, kH16BigFull = false;
+  static constexpr int kH16BigWaves = 8;
   struct Job {
     float* out;
     uint16_t* out16;     // optional 16-bit copy of b (operand of the next product)
