@@ -269,7 +269,14 @@ def main(argv=None):
         mfma_flops = nf * executed
         bf = cfg.prec == capi.BF16_IN
         peak = PEAK_BF16_MFMA if bf else PEAK_F32_MFMA
-        kname = ("gemm_h16_nt_kernel<EpiClenshaw, bf16>" if bf else f32_kernel + "<EpiClenshaw>") + \
+        if bf and B % 256 == 0:
+            # 4 x 2 waves of 64 x 128: on a diagonal tile the 2 waves wholly below it idle
+            t = B // 256
+            mfma_flops = nf * 2.0 * B ** 3 * (t * (t - 1) / 2 + t * 6 / 8) / t ** 2
+            h16_kernel = "gemm_h16_big_kernel<EpiClenshaw, bf16, 8 waves>"
+        else:
+            h16_kernel = "gemm_h16_nt_kernel<EpiClenshaw, bf16>"
+        kname = (h16_kernel if bf else f32_kernel + "<EpiClenshaw>") + \
             " (one symmetric Clenshaw product per factor, upper tiles)"
     cap = max(1, per_step * refreshes)
     kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]
