@@ -166,15 +166,19 @@ def test_newton_matches_oracle(B, variant, p, iters, full):
     report("newton", B=B, variant=variant, p=p, iters=iters, full=full, err=err)
 
 
-@pytest.mark.parametrize("B", [512, 768])
-@pytest.mark.parametrize("solver,variant,arg,full", [("newton", capi.NDB_Z, 6, False), ("newton", capi.NDB, 6, False),
-                                                     ("newton", capi.NDB_Z, 6, True), ("newton", capi.CN, 6, False),
-                                                     ("cheby", None, 16, False)])
+SPAN_CASES = [("newton", capi.NDB_Z, 6, False), ("newton", capi.NDB, 6, False), ("newton", capi.NDB_Z, 6, True),
+              ("newton", capi.CN, 6, False), ("cheby", None, 16, False)]
+
+
+@pytest.mark.parametrize("B,solver,variant,arg,full",
+                         [(B,) + c for B in (512, 768) for c in SPAN_CASES] +
+                         [(1280,) + SPAN_CASES[0], (1280,) + SPAN_CASES[4]])
 def test_fp32_products_span_tiles(B, solver, variant, arg, full):
     """fp32 roots on several output tiles per factor: B = 512 runs the 256 x 256
     direct-to-LDS kernel on 2 x 2 tiles (3 upper tiles, two of them diagonal),
-    B = 768 the 128 x 128 kernel on 6 x 6 tiles; symmetric and full products,
-    reductions and epilogues all cross tile boundaries."""
+    B = 1280 on 5 x 5 (15 upper tiles), B = 768 the 128 x 128 kernel on 6 x 6
+    tiles; symmetric and full products, reductions and epilogues all cross
+    tile boundaries."""
     nf = 3
     F = W.spd_factors(70 + B, nf, B, cond=1e3)
     V0 = W.start_vectors(71, nf, B)
@@ -361,10 +365,11 @@ def test_coupled_newton_fp16_matches_oracle(B, p, iters, full):
     report("cn_fp16", B=B, p=p, iters=iters, full=full, err=err)
 
 
-@pytest.mark.parametrize("B", [384, 512])
+@pytest.mark.parametrize("B", [384, 512, 1280])
 def test_half_width_products_span_tiles(B):
     """The 16-bit products on several tiles per factor: B = 384 runs the
-    128 x 128 workgroup tile (3 x 3 tiles), B = 512 the 256 x 256 one (2 x 2),
+    128 x 128 workgroup tile (3 x 3 tiles), B = 512 and 1280 the 256 x 256 ones
+    (2 x 2 and 5 x 5),
     both with off-diagonal symmetric tiles and their mirrored writes:
     bf16-input accumulation, Chebyshev (symmetric and full products), coupled
     Newton on fp16 operands (with its tile reductions) and preconditioning."""
