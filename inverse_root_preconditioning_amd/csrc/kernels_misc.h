@@ -247,6 +247,139 @@ __global__ void __launch_bounds__(256, 2) pi_step_kernel(const PiArgs P) {
   }
 }
 
+// The same step for 128-row panels when V has 32 columns per row (every step
+// after the first): F and V go straight into LDS (global_load_lds_dwordx4)
+// through a ring of three 32-deep stages, two stages ahead of the MFMAs, with
+// one barrier per stage.  F is stored [row][8 quads of 4 k] with the quad index
+// XOR-ed by (row ^ (row >> 3)) & 7 (conflict-free fragment reads on 64 banks),
+// V as [k][32].  The arithmetic and its order are those of pi_step_kernel<128>.
+__global__ void __launch_bounds__(256, 2) pi_step_dma_kernel(const PiArgs P) {
+  constexpr int PANEL = 128, BK = 32;
+  constexpr int kF = PANEL * BK, kV = BK * kPiCols, kStage = kF + kV;  // floats
+  constexpr int NL = 5;                                                  // loads per thread and stage
+  constexpr int kWaitAhead = NL | (7 << 4);                              // vmcnt(5) lgkmcnt(0)
+  // One LDS object (see gemm_f32_big_kernel): the ring, then s_col and the column sums.
+  __shared__ __attribute__((aligned(16))) float lds[3 * kStage + kPiCols + 2 * 4 * kPiCols];
+  float* const s_col = lds + 3 * kStage;
+  float* const colsum = s_col + kPiCols;  // [2][4 row blocks][32]
+  const uint32_t lid = xcd_remap(blockIdx.x, P.total);
+  const int64_t f = lid / P.npanels;
+  const int panel = lid - (uint32_t)f * P.npanels;
+  const int m0 = panel * PANEL;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < kPiCols) {
+    const int j = tid;
+    float s = 0.f;
+    if (j < P.r) {
+      if (P.norm_in == nullptr) {
+        s = 1.f;
+      } else {
+        float n2 = 0.f;
+        for (int p = 0; p < P.npanels; ++p) n2 += P.norm_in[(f * P.npanels + p) * kPiCols + j];
+        s = (n2 > 0.f) ? 1.f / sqrtf(n2) : ((n2 == 0.f) ? 0.f : n2);  // NaN propagates
+      }
+    }
+    s_col[j] = s;
+  }
+  const int B = P.B;
+  const float* Fp = P.F + f * (int64_t)B * B;
+  const float* Vp = P.vin + f * (int64_t)B * kPiCols;
+  auto swz = [](int row) { return (row ^ (row >> 3)) & 7; };
+  // F: 4 pieces per thread and stage (wave instruction it * 4 + wave covers rows 8 (it * 4 + wave) ..);
+  // V: one piece (row tid / 8, columns 4 (tid % 8) ..)
+  const float* srcF[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int row = (it * 4 + wave) * 8 + (lane >> 3);
+    srcF[it] = Fp + (int64_t)(m0 + row) * B + 4 * ((lane & 7) ^ swz(row));
+  }
+  const float* srcV = Vp + (int64_t)(tid >> 3) * kPiCols + 4 * (tid & 7);
+  const int nstages = B / BK;
+  auto issue = [&](float* __restrict__ buf, int s) __attribute__((always_inline)) {
+    const int k0 = min(s, nstages - 1) * BK;  // past the end: the last stage again, never read
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcF[it] + k0),
+                                       (__attribute__((address_space(3))) void*)(buf + (it * 4 + wave) * 64 * 4),
+                                       16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcV + (int64_t)k0 * kPiCols),
+                                     (__attribute__((address_space(3))) void*)(buf + kF + wave * 64 * 4), 16, 0, 0);
+  };
+  floatx16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  float* const b0 = lds;
+  float* const b1 = lds + kStage;
+  float* const b2 = lds + 2 * kStage;
+  issue(b0, 0);
+  issue(b1, 1);
+  __builtin_amdgcn_s_waitcnt(kWaitAhead);
+  __builtin_amdgcn_s_barrier();
+  auto step = [&](const float* __restrict__ rd, float* __restrict__ wr, int s) __attribute__((always_inline)) {
+    issue(wr, s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    const int row = wave * 32 + (lane & 31);
+#pragma unroll
+    for (int g = 0; g < BK / 8; ++g) {
+      const int quad = 2 * g + (lane >> 5);
+      const floatx4 fa = *reinterpret_cast<const floatx4*>(rd + row * BK + 4 * (quad ^ swz(row)));
+      const float* vq = rd + kF + (8 * g + 4 * (lane >> 5)) * kPiCols + (lane & 31);
+      floatx4 fv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fv[e] = vq[e * kPiCols];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[q], fv[q], acc, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitAhead);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  int s = 0;
+  for (; s + 3 <= nstages; s += 3) {
+    step(b0, b2, s);
+    step(b1, b0, s + 1);
+    step(b2, b1, s + 2);
+  }
+  if (s < nstages) step(b0, b2, s);
+  if (s + 1 < nstages) step(b1, b0, s + 1);
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // the loads issued past the end
+
+  const int j = lane & 31;
+  const float sj = s_col[j];
+  const float eps = P.sc[f].eps;
+  float nsum = 0.f, rsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = m0 + wave * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+    const float v = (j < P.r) ? ldg(Vp + (int64_t)row * kPiCols + j) * sj : 0.f;
+    const float w = acc[e] * sj + eps * v;
+    if (!P.last) stg(P.wout + (f * B + row) * kPiCols + j, w);
+    nsum += w * w;
+    rsum += v * w;
+  }
+  nsum += __shfl_xor(nsum, 32, kWave);
+  rsum += __shfl_xor(rsum, 32, kWave);
+  if (lane < 32) {
+    colsum[wave * kPiCols + j] = nsum;
+    colsum[(4 + wave) * kPiCols + j] = rsum;
+  }
+  __syncthreads();
+  if (tid < kPiCols) {
+    const int c = tid;
+    const int64_t o = (f * P.npanels + panel) * kPiCols + c;
+    float n = 0.f, q = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      n += colsum[b * kPiCols + c];
+      q += colsum[(4 + b) * kPiCols + c];
+    }
+    P.norm_out[o] = n;
+    if (P.last) P.rq_out[o] = q;
+  }
+}
+
 // One wave per factor: lambda = max_j q_j, c = safety lambda, status bits.
 __global__ void __launch_bounds__(64) pi_finalize_kernel(const float* __restrict__ rq, int npanels, int r,
                                                         float safety, shampoo_scale* __restrict__ sc,

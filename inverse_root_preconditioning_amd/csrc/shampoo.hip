@@ -1068,7 +1068,9 @@ int shampoo_scale_power(const float* factors, int64_t nfactors, int B, float eps
     P.norm_in = (t == 0) ? nullptr : w.norm[(t - 1) & 1];
     P.norm_out = w.norm[t & 1];
     P.last = (t == steps) ? 1 : 0;
-    if (panel == 128)
+    if (panel == 128 && P.ldv == kPiCols)
+      hipLaunchKernelGGL(pi_step_dma_kernel, dim3(P.total), dim3(256), 0, stream, P);
+    else if (panel == 128)
       hipLaunchKernelGGL(pi_step_kernel<128>, dim3(P.total), dim3(256), 0, stream, P);
     else
       hipLaunchKernelGGL(pi_step_kernel<64>, dim3(P.total), dim3(256), 0, stream, P);
