@@ -594,9 +594,30 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
   }
   __syncthreads();  // every load has landed (each stage ended with vmcnt(0)); the epilogue may reuse LDS
 
-  gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM, WAVES == 16 ? 1 : 8>(P, job, item, tm, tn, acc,
-                                                                   reinterpret_cast<float*>(lds), red, m0, n0, wm,
-                                                                   wn, lane, mask);
+  // The 8-wave layout runs epilogues other than the register-direct symmetric
+  // one through LDS (staged_epilogue), so that no accumulator register is live
+  // while their loads are in flight; its idle waves hold zeros, which that
+  // path neither writes below the diagonal nor counts.
+  constexpr bool kDirectSym = [] {
+    if constexpr (Epi::kSym) return Epi::kDirect && !Epi::kReduce && SYM;
+    return false;
+  }();
+  if constexpr (WAVES == 8 && !kDirectSym) {
+    typename Epi::Tile tile(*(job == 0 ? &P.e[0] : &P.e[1]), item, P.B);
+    const float part = staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, reinterpret_cast<float*>(lds), m0,
+                                                                    n0, wm, wn, lane, SYM, tm == tn);
+    if constexpr (Epi::kReduce) {
+      const float tot = block_sum<NT>(part, red);
+      if (threadIdx.x == 0) {
+        tile.partial(tm * P.tiles_n + tn, tot);
+        if (SYM && tm != tn) tile.partial(tn * P.tiles_n + tm, tot);  // the mirrored tile
+      }
+    }
+  } else {
+    gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM, WAVES == 16 ? 1 : 8>(P, job, item, tm, tn, acc,
+                                                                     reinterpret_cast<float*>(lds), red, m0, n0, wm,
+                                                                     wn, lane, mask);
+  }
 }
 
 template <class Epi>

@@ -850,8 +850,9 @@ struct EpiCnM {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = false;
   static constexpr bool kBigSym = false, kBigFull = false;
-  static constexpr bool kH16BigSym = false, kH16BigFull = false;
-  static constexpr int kH16BigWaves = 16;
+  // 16-bit: the 8-wave layout with its epilogue through LDS
+  static constexpr bool kH16BigSym = true, kH16BigFull = true;
+  static constexpr int kH16BigWaves = 8;
   static constexpr bool kReduce = true;
   struct Job {
     float* m;            // fp32 outputs (null: not written)
