@@ -614,7 +614,9 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
       }
     }
   } else {
-    gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM, WAVES == 16 ? 1 : 8>(P, job, item, tm, tn, acc,
+    constexpr int SP = WAVES == 16 ? 1 : 2;  // mirrored half staged per block (16 waves) or block pair (8)
+    static_assert(NT / kWave * 32 * (32 * SP + 4) + NT / kWave <= kFloats, "staging and reduction fit the buffers");
+    gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM, WAVES == 16 ? 1 : 8, SP>(P, job, item, tm, tn, acc,
                                                                      reinterpret_cast<float*>(lds), red, m0, n0, wm,
                                                                      wn, lane, mask);
   }

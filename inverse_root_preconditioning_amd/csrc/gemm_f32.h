@@ -218,13 +218,26 @@ __device__ __forceinline__ float sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN
 // store (on a diagonal tile only those strictly below the diagonal).  Only
 // the 32 x 32 blocks (i, j) with bit i TN + j of `mask` set are written.
 // KPRE bounds how many groups' epilogue inputs are loaded ahead (registers).
-template <int TM, int TN, int KPRE, class Tile>
+//
+// SP > 0 (off-diagonal tiles only): the mirrored half goes through `stage`,
+// this wave's 32 x (32 SP + 4) floats of LDS.  Each group is first written
+// there at its transposed place; once SP vertically adjacent blocks are in,
+// the wave reads them back along the mirrored rows and each store instruction
+// covers 32 SP consecutive columns of 64 / (8 SP) rows (whole 128-byte lines,
+// where a register-direct mirrored store covers 32 bytes of 32 rows).  Groups
+// are then taken column of blocks by column of blocks (j-major).
+template <int TM, int TN, int KPRE, int SP = 0, class Tile>
 __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[TM][TN], int m0, int n0, int wm,
-                                                    int wn, int lane, bool diag, int mask) {
+                                                    int wn, int lane, bool diag, int mask, float* stage = nullptr) {
+  static_assert(SP == 0 || (TM % SP == 0 && SP <= 2), "staged blocks per column");
+  constexpr int LDT = 32 * SP + 4;  // staged row pitch in floats: the group writes of 16 lanes hit 64 banks
   const int h = lane >> 5, cl = lane & 31;
-  // Forms and writes group G (block i, j; accumulators 4 q .. 4 q + 3).
+  // group G -> block (i, j), accumulators 4 q .. 4 q + 3
+  auto gi_ = [](int g) { return SP ? (g / 4) % TM : g / (TN * 4); };
+  auto gj_ = [](int g) { return SP ? g / (TM * 4) : (g / 4) % TN; };
+  // Forms and writes group G.
   auto emit = [&](auto G, const auto& o) __attribute__((always_inline)) {
-    constexpr int i = decltype(G)::value / (TN * 4), j = (decltype(G)::value / 4) % TN, q = decltype(G)::value % 4;
+    constexpr int i = gi_(decltype(G)::value), j = gj_(decltype(G)::value), q = decltype(G)::value % 4;
     const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
     const int c = n0 + wn + 32 * j + cl;
 #pragma unroll
@@ -238,28 +251,56 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
         if (r + e < c) tile.write(c, r + e, o[e]);
     }
   };
+  // Off-diagonal tile with staging: the upper entries directly, the mirrored
+  // ones into `stage`; after the last group of SP blocks of one column, the
+  // staged (32 SP) x 32 block is written along its mirrored rows.
+  auto emit_staged = [&](auto G, const auto& o) __attribute__((always_inline)) {
+    if constexpr (SP > 0) {
+    constexpr int g = decltype(G)::value;
+    constexpr int i = gi_(g), j = gj_(g), q = g % 4;
+    const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
+    const int c = n0 + wn + 32 * j + cl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile.write_upper(r + e, c, o[e]);
+    *reinterpret_cast<floatx4*>(stage + cl * LDT + 32 * (i % SP) + 8 * q + 4 * h) = o;
+    if constexpr (q == 3 && i % SP == SP - 1) {
+      __builtin_amdgcn_wave_barrier();
+      constexpr int LPR = 8 * SP;  // lanes per staged row
+      constexpr int RPI = 64 / LPR;  // rows per instruction
+      const int rr = lane / LPR, cc = 4 * (lane % LPR);
+      const int c0 = n0 + wn + 32 * j, r0 = m0 + wm + 32 * (i - (SP - 1));
+#pragma unroll
+      for (int t = 0; t < 32 / RPI; ++t) {
+        const int row = RPI * t + rr;
+        tile.write4t(c0 + row, r0 + cc, *reinterpret_cast<const floatx4*>(stage + row * LDT + cc));
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    }
+  };
   auto rc = [&](auto G, int& r, int& c) __attribute__((always_inline)) {
-    constexpr int i = decltype(G)::value / (TN * 4), j = (decltype(G)::value / 4) % TN, q = decltype(G)::value % 4;
+    constexpr int i = gi_(decltype(G)::value), j = gj_(decltype(G)::value), q = decltype(G)::value % 4;
     r = m0 + wm + 32 * i + 8 * q + 4 * h;
     c = n0 + wn + 32 * j + cl;
   };
   auto acc4 = [&](auto G) __attribute__((always_inline)) {
-    constexpr int i = decltype(G)::value / (TN * 4), j = (decltype(G)::value / 4) % TN, q = decltype(G)::value % 4;
+    constexpr int i = gi_(decltype(G)::value), j = gj_(decltype(G)::value), q = decltype(G)::value % 4;
     return floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
   };
   auto computed = [&](auto G) __attribute__((always_inline)) {
-    constexpr int i = decltype(G)::value / (TN * 4), j = (decltype(G)::value / 4) % TN;
+    constexpr int i = gi_(decltype(G)::value), j = gj_(decltype(G)::value);
     return ((mask >> (i * TN + j)) & 1) != 0;  // a block this wave computed
   };
   // groups prefetched together: at most the epilogue's wish, the caller's register budget and the groups there are
   constexpr int K0 = Tile::kPrefetch < KPRE ? Tile::kPrefetch : KPRE;
   constexpr int K = K0 < TM * TN * 4 ? K0 : TM * TN * 4;
+  auto body = [&](auto&& out) __attribute__((always_inline)) {
   if constexpr (K == 0) {
     static_for<TM * TN * 4>([&](auto G) __attribute__((always_inline)) {
       if (!computed(G)) return;
       int r, c;
       rc(G, r, c);
-      emit(G, tile.value4(r, c, acc4(G)));
+      out(G, tile.value4(r, c, acc4(G)));
     });
   } else {
     // The epilogue's own inputs are requested a chunk of K groups at a time,
@@ -287,10 +328,18 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
         if (!computed(gi)) return;
         int r, c;
         rc(gi, r, c);
-        emit(gi, tile.value4p(r, c, acc4(gi), pre[decltype(C)::value & 1][decltype(G)::value]));
+        out(gi, tile.value4p(r, c, acc4(gi), pre[decltype(C)::value & 1][decltype(G)::value]));
       });
     });
   }
+  };
+  if constexpr (SP > 0) {
+    if (!diag) {
+      body(emit_staged);
+      return;
+    }
+  }
+  body(emit);
 }
 
 // Workgroup lid -> (job, item, tile row tm, tile column tn), item-major: the
@@ -326,8 +375,11 @@ __device__ __forceinline__ void decode_tile(const L& P, uint32_t lid, int& job, 
 // wave's (32 TM) x (32 TN) part, at (wm, wn) in the tile at (m0, n0).  `lds`
 // must hold (BM / PH) x (BN + 1) floats and be free; `red` NT / 64 floats.
 // `mask` (the blocks this wave computed) is honoured by the register-direct
-// symmetric epilogue; the other paths need every block computed.
-template <int TM, int TN, int BM, int BN, int NT, int PH, bool SYM, int KPRE = (NT == kGemmThreads ? 2 : 1), class L>
+// symmetric epilogue; the other paths need every block computed.  SP > 0
+// stages that epilogue's mirrored half (see sym_epilogue_direct): `lds` must
+// then also hold NT / 64 x 32 x (32 SP + 4) floats.
+template <int TM, int TN, int BM, int BN, int NT, int PH, bool SYM, int KPRE = (NT == kGemmThreads ? 2 : 1),
+          int SP = 0, class L>
 __device__ __forceinline__ void gemm_epilogue(const L& P, int job, int64_t item, int tm, int tn,
                                               floatx16 (&acc)[TM][TN], float* lds, float* red, int m0, int n0,
                                               int wm, int wn, int lane, int mask = (1 << (TM * TN)) - 1) {
@@ -336,8 +388,12 @@ __device__ __forceinline__ void gemm_epilogue(const L& P, int job, int64_t item,
   float part = 0.f;
   bool done = false;
   if constexpr (Epi::kSym && SYM) {
-    if constexpr (Epi::kDirect && !Epi::kReduce)
-      sym_epilogue_direct<TM, TN, KPRE>(tile, acc, m0, n0, wm, wn, lane, tm == tn, mask);
+    if constexpr (Epi::kDirect && !Epi::kReduce) {
+      // waves of 1024-thread workgroups (128 VGPRs) have no room for staging beside loads ahead
+      constexpr int kSP = (NT >= 1024 && Epi::Tile::kPrefetch > 0) ? 0 : SP;
+      sym_epilogue_direct<TM, TN, KPRE, kSP>(tile, acc, m0, n0, wm, wn, lane, tm == tn, mask,
+                                             lds + (threadIdx.x / kWave) * 32 * (32 * kSP + 4));
+    }
     else
       part = sym_epilogue<TM, TN, BM, BN, NT, PH, Epi::kReduce>(tile, acc, lds, m0, n0, wm, wn, lane, tm == tn);
     done = true;
@@ -679,7 +735,9 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __syncthreads();
 
-  gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM>(P, job, item, tm, tn, acc, lds, red, m0, n0, wm, wn, lane, mask);
+  // mirrored half of symmetric tiles staged per 32 x 32 block (16 waves x 4.5 KB of the stage buffers)
+  static_assert(NT / kWave * 32 * 36 + NT / kWave <= 3 * kStage, "staging and reduction fit the buffers");
+  gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM, 1, 1>(P, job, item, tm, tn, acc, lds, red, m0, n0, wm, wn, lane, mask);
 }
 
 // ---------------------------------------------------------------------------
