@@ -256,26 +256,26 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
   // staged (32 SP) x 32 block is written along its mirrored rows.
   auto emit_staged = [&](auto G, const auto& o) __attribute__((always_inline)) {
     if constexpr (SP > 0) {
-    constexpr int g = decltype(G)::value;
-    constexpr int i = gi_(g), j = gj_(g), q = g % 4;
-    const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
-    const int c = n0 + wn + 32 * j + cl;
+      constexpr int g = decltype(G)::value;
+      constexpr int i = gi_(g), j = gj_(g), q = g % 4;
+      const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
+      const int c = n0 + wn + 32 * j + cl;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tile.write_upper(r + e, c, o[e]);
-    *reinterpret_cast<floatx4*>(stage + cl * LDT + 32 * (i % SP) + 8 * q + 4 * h) = o;
-    if constexpr (q == 3 && i % SP == SP - 1) {
-      __builtin_amdgcn_wave_barrier();
-      constexpr int LPR = 8 * SP;  // lanes per staged row
-      constexpr int RPI = 64 / LPR;  // rows per instruction
-      const int rr = lane / LPR, cc = 4 * (lane % LPR);
-      const int c0 = n0 + wn + 32 * j, r0 = m0 + wm + 32 * (i - (SP - 1));
+      for (int e = 0; e < 4; ++e) tile.write_upper(r + e, c, o[e]);
+      *reinterpret_cast<floatx4*>(stage + cl * LDT + 32 * (i % SP) + 8 * q + 4 * h) = o;
+      if constexpr (q == 3 && i % SP == SP - 1) {
+        __builtin_amdgcn_wave_barrier();
+        constexpr int LPR = 8 * SP;  // lanes per staged row
+        constexpr int RPI = 64 / LPR;  // rows per instruction
+        const int rr = lane / LPR, cc = 4 * (lane % LPR);
+        const int c0 = n0 + wn + 32 * j, r0 = m0 + wm + 32 * (i - (SP - 1));
 #pragma unroll
-      for (int t = 0; t < 32 / RPI; ++t) {
-        const int row = RPI * t + rr;
-        tile.write4t(c0 + row, r0 + cc, *reinterpret_cast<const floatx4*>(stage + row * LDT + cc));
+        for (int t = 0; t < 32 / RPI; ++t) {
+          const int row = RPI * t + rr;
+          tile.write4t(c0 + row, r0 + cc, *reinterpret_cast<const floatx4*>(stage + row * LDT + cc));
+        }
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_wave_barrier();
-    }
     }
   };
   auto rc = [&](auto G, int& r, int& c) __attribute__((always_inline)) {
@@ -295,43 +295,43 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
   constexpr int K0 = Tile::kPrefetch < KPRE ? Tile::kPrefetch : KPRE;
   constexpr int K = K0 < TM * TN * 4 ? K0 : TM * TN * 4;
   auto body = [&](auto&& out) __attribute__((always_inline)) {
-  if constexpr (K == 0) {
-    static_for<TM * TN * 4>([&](auto G) __attribute__((always_inline)) {
-      if (!computed(G)) return;
-      int r, c;
-      rc(G, r, c);
-      out(G, tile.value4(r, c, acc4(G)));
-    });
-  } else {
-    // The epilogue's own inputs are requested a chunk of K groups at a time,
-    // one chunk ahead of the groups being formed and written (stores in
-    // between would otherwise keep each load behind the previous group's
-    // stores, one memory latency per group).
-    constexpr int NC = TM * TN * 4 / K;
-    static_assert(NC * K == TM * TN * 4, "whole chunks");
-    typename Tile::Pre pre[2][K];
-    auto fetch = [&](auto C) __attribute__((always_inline)) {
-      static_for<K>([&](auto G) __attribute__((always_inline)) {
-        constexpr int g = decltype(C)::value * K + decltype(G)::value;
-        if (!computed(std::integral_constant<int, g>{})) return;
+    if constexpr (K == 0) {
+      static_for<TM * TN * 4>([&](auto G) __attribute__((always_inline)) {
+        if (!computed(G)) return;
         int r, c;
-        rc(std::integral_constant<int, g>{}, r, c);
-        pre[decltype(C)::value & 1][decltype(G)::value] = tile.prefetch4(r, c);
+        rc(G, r, c);
+        out(G, tile.value4(r, c, acc4(G)));
       });
-    };
-    fetch(std::integral_constant<int, 0>{});
-    static_for<NC>([&](auto C) __attribute__((always_inline)) {
-      if constexpr (decltype(C)::value + 1 < NC) fetch(std::integral_constant<int, decltype(C)::value + 1>{});
-      static_for<K>([&](auto G) __attribute__((always_inline)) {
-        constexpr int g = decltype(C)::value * K + decltype(G)::value;
-        const std::integral_constant<int, g> gi{};
-        if (!computed(gi)) return;
-        int r, c;
-        rc(gi, r, c);
-        out(gi, tile.value4p(r, c, acc4(gi), pre[decltype(C)::value & 1][decltype(G)::value]));
+    } else {
+      // The epilogue's own inputs are requested a chunk of K groups at a time,
+      // one chunk ahead of the groups being formed and written (stores in
+      // between would otherwise keep each load behind the previous group's
+      // stores, one memory latency per group).
+      constexpr int NC = TM * TN * 4 / K;
+      static_assert(NC * K == TM * TN * 4, "whole chunks");
+      typename Tile::Pre pre[2][K];
+      auto fetch = [&](auto C) __attribute__((always_inline)) {
+        static_for<K>([&](auto G) __attribute__((always_inline)) {
+          constexpr int g = decltype(C)::value * K + decltype(G)::value;
+          if (!computed(std::integral_constant<int, g>{})) return;
+          int r, c;
+          rc(std::integral_constant<int, g>{}, r, c);
+          pre[decltype(C)::value & 1][decltype(G)::value] = tile.prefetch4(r, c);
+        });
+      };
+      fetch(std::integral_constant<int, 0>{});
+      static_for<NC>([&](auto C) __attribute__((always_inline)) {
+        if constexpr (decltype(C)::value + 1 < NC) fetch(std::integral_constant<int, decltype(C)::value + 1>{});
+        static_for<K>([&](auto G) __attribute__((always_inline)) {
+          constexpr int g = decltype(C)::value * K + decltype(G)::value;
+          const std::integral_constant<int, g> gi{};
+          if (!computed(gi)) return;
+          int r, c;
+          rc(gi, r, c);
+          out(gi, tile.value4p(r, c, acc4(gi), pre[decltype(C)::value & 1][decltype(G)::value]));
+        });
       });
-    });
-  }
+    }
   };
   if constexpr (SP > 0) {
     if (!diag) {
