@@ -255,7 +255,8 @@ def main(argv=None):
         mfma_flops = flops_per_launch
         half = base_variant == capi.CN_F16
         peak = PEAK_BF16_MFMA if half else PEAK_F32_MFMA
-        kname = ("gemm_h16_nt_kernel<EpiCnM, fp16>" if half else "gemm_f32_kernel<EpiCnM>") + \
+        h16_cn = "gemm_h16_big_kernel<EpiCnM, fp16, 8 waves>" if B % 256 == 0 else "gemm_h16_nt_kernel<EpiCnM, fp16>"
+        kname = (h16_cn if half else "gemm_f32_kernel<EpiCnM>") + \
             " (coupled Newton C^p M, one full product per factor)"
     elif cfg.solver == "newton":
         family, per_step = capi.TIME_NDB_PAIR, 2 * (cfg.iters - 2)
@@ -270,9 +271,7 @@ def main(argv=None):
         bf = cfg.prec == capi.BF16_IN
         peak = PEAK_BF16_MFMA if bf else PEAK_F32_MFMA
         if bf and B % 256 == 0:
-            # 4 x 2 waves of 64 x 128: on a diagonal tile the 2 waves wholly below it idle
-            t = B // 256
-            mfma_flops = nf * 2.0 * B ** 3 * (t * (t - 1) / 2 + t * 6 / 8) / t ** 2
+            # 4 x 2 waves of 64 x 128; a diagonal tile computes its 36 upper 32 x 32 blocks (9/16)
             h16_kernel = "gemm_h16_big_kernel<EpiClenshaw, bf16, 8 waves>"
         else:
             h16_kernel = "gemm_h16_nt_kernel<EpiClenshaw, bf16>"

@@ -437,6 +437,33 @@ static inline int bf16_gather(const shampoo_block* d, int64_t n, int B, uint16_t
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int h16_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
+// 8 waves of 64 x 128 on a 256 x 256 tile: wave w takes block row r (64
+// rows) and column half c (128 columns) from a fixed placement.  On a
+// diagonal tile of a symmetric product a wave computes only its 32 x 32
+// blocks (bit 4 i + j for block row i, column j) on or above the diagonal,
+// and waves 4 and 5, whose placements lie wholly below it, each take one
+// block from waves 2 and 3 (at their placements), so that the two waves of
+// every SIMD (w and w + 4 share one) compute 9 of the tile's 36 upper blocks.
+// Off-diagonal tiles: every wave computes its whole 64 x 128 block.
+constexpr uint32_t kH16Place8 = 0x27645031u;  // 4 bits 2 r + c per wave, w = 0 in the low bits
+constexpr int kH16Donated = 0x80;             // block (1, 3) of waves 2 and 3, computed by waves 4 and 5
+__device__ __forceinline__ void h16_wave_role8(bool dtile, int wave, int& wm, int& wn, int& mask) {
+  const bool helper = dtile && (wave == 4 || wave == 5);
+  const int place = (int)((kH16Place8 >> (4 * (helper ? wave - 2 : wave))) & 15);
+  const int r = place >> 1, c = place & 1;
+  wm = 64 * r;
+  wn = 128 * c;
+  mask = 0xFF;
+  if (dtile) {
+    mask = 0;
+    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 4; ++j)
+        if (4 * c + j >= 2 * r + i) mask |= 1 << (4 * i + j);
+    if (wave == 2 || wave == 3) mask &= ~kH16Donated;
+    if (helper) mask = kH16Donated;
+  }
+}
+
 // WAVES = 16: 4 x 4 waves of 64 x 64 (128 VGPRs each).  WAVES = 8: 4 x 2 waves
 // of 64 x 128 (256 VGPRs each), for epilogues that want registers to load
 // ahead; on a diagonal tile of a symmetric product its waves wholly below
@@ -469,9 +496,19 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // The 8-wave layout runs epilogues other than the register-direct symmetric
+  // one through LDS (staged_epilogue), so that no accumulator register is live
+  // while their loads are in flight; its idle waves hold zeros, which that
+  // path neither writes below the diagonal nor counts.
+  constexpr bool kDirectSym = [] {
+    if constexpr (Epi::kSym) return Epi::kDirect && !Epi::kReduce && SYM;
+    return false;
+  }();
   int wm, wn, mask;
   if constexpr (WAVES == 16) {
     big_wave_role(SYM && tm == tn, wave, wm, wn, mask);
+  } else if constexpr (kDirectSym) {
+    h16_wave_role8(tm == tn, wave, wm, wn, mask);
   } else {
     wm = (wave >> 1) * 64;
     wn = (wave & 1) * 128;
@@ -584,6 +621,13 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
       case 0x8: mainloop(std::integral_constant<int, 0x8>{}); break;
       default: mainloop(std::integral_constant<int, 0>{}); break;
     }
+  } else if constexpr (SYM && kDirectSym) {
+    switch (mask) {  // the masks h16_wave_role8 hands out
+      case 0xFF: mainloop(std::integral_constant<int, 0xFF>{}); break;
+      case 0x6F: mainloop(std::integral_constant<int, 0x6F>{}); break;
+      case 0x8C: mainloop(std::integral_constant<int, 0x8C>{}); break;
+      default: mainloop(std::integral_constant<int, kH16Donated>{}); break;
+    }
   } else if constexpr (SYM) {
     if (mask)
       mainloop(std::integral_constant<int, kFull>{});
@@ -594,14 +638,6 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
   }
   __syncthreads();  // every load has landed (each stage ended with vmcnt(0)); the epilogue may reuse LDS
 
-  // The 8-wave layout runs epilogues other than the register-direct symmetric
-  // one through LDS (staged_epilogue), so that no accumulator register is live
-  // while their loads are in flight; its idle waves hold zeros, which that
-  // path neither writes below the diagonal nor counts.
-  constexpr bool kDirectSym = [] {
-    if constexpr (Epi::kSym) return Epi::kDirect && !Epi::kReduce && SYM;
-    return false;
-  }();
   if constexpr (WAVES == 8 && !kDirectSym) {
     typename Epi::Tile tile(*(job == 0 ? &P.e[0] : &P.e[1]), item, P.B);
     const float part = staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, reinterpret_cast<float*>(lds), m0,

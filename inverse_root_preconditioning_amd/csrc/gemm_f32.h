@@ -219,13 +219,14 @@ __device__ __forceinline__ float sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN
 // the 32 x 32 blocks (i, j) with bit i TN + j of `mask` set are written.
 // KPRE bounds how many groups' epilogue inputs are loaded ahead (registers).
 //
-// SP > 0 (off-diagonal tiles only): the mirrored half goes through `stage`,
-// this wave's 32 x (32 SP + 4) floats of LDS.  Each group is first written
-// there at its transposed place; once SP vertically adjacent blocks are in,
-// the wave reads them back along the mirrored rows and each store instruction
-// covers 32 SP consecutive columns of 64 / (8 SP) rows (whole 128-byte lines,
-// where a register-direct mirrored store covers 32 bytes of 32 rows).  Groups
-// are then taken column of blocks by column of blocks (j-major).
+// SP > 0: the mirrored half goes through `stage`, this wave's 32 x (32 SP + 4)
+// floats of LDS.  Each group is first written there at its transposed place;
+// once the SP vertically adjacent blocks of one column are in, the wave reads
+// them back along the mirrored rows and each store instruction covers 32 SP
+// consecutive columns of 64 / (8 SP) rows (whole 128-byte lines, where a
+// register-direct mirrored store covers 32 bytes of 32 rows).  On a diagonal
+// tile only entries of computed blocks strictly below the diagonal go out.
+// Groups are then taken column of blocks by column of blocks (j-major).
 template <int TM, int TN, int KPRE, int SP = 0, class Tile>
 __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[TM][TN], int m0, int n0, int wm,
                                                     int wn, int lane, bool diag, int mask, float* stage = nullptr) {
@@ -251,28 +252,52 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
         if (r + e < c) tile.write(c, r + e, o[e]);
     }
   };
-  // Off-diagonal tile with staging: the upper entries directly, the mirrored
-  // ones into `stage`; after the last group of SP blocks of one column, the
-  // staged (32 SP) x 32 block is written along its mirrored rows.
-  auto emit_staged = [&](auto G, const auto& o) __attribute__((always_inline)) {
+  // Staged: the upper entries directly, the group into `stage`.  DG: a
+  // diagonal tile (compile-time, so that off-diagonal tiles carry no tests).
+  auto emit_staged = [&](auto DG, auto G, const auto& o) __attribute__((always_inline)) {
     if constexpr (SP > 0) {
       constexpr int g = decltype(G)::value;
       constexpr int i = gi_(g), j = gj_(g), q = g % 4;
       const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
       const int c = n0 + wn + 32 * j + cl;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tile.write_upper(r + e, c, o[e]);
+      for (int e = 0; e < 4; ++e)
+        if (!decltype(DG)::value || r + e <= c) tile.write_upper(r + e, c, o[e]);
       *reinterpret_cast<floatx4*>(stage + cl * LDT + 32 * (i % SP) + 8 * q + 4 * h) = o;
+    }
+  };
+  // After the last group of the SP blocks of one column, computed or not: the
+  // staged (32 SP) x 32 block goes out along its mirrored rows.
+  auto flush = [&](auto DG, auto G) __attribute__((always_inline)) {
+    if constexpr (SP > 0) {
+      constexpr int g = decltype(G)::value;
+      constexpr int i = gi_(g), j = gj_(g), q = g % 4;
       if constexpr (q == 3 && i % SP == SP - 1) {
+        constexpr int i0 = i - (SP - 1);
+        constexpr int kUnit = SP == 2 ? (1 | (1 << TN)) : 1;  // blocks (i0, 0) .. (i, 0) as mask bits
+        if (decltype(DG)::value && (mask & (kUnit << (i0 * TN + j))) == 0) return;  // none computed here
         __builtin_amdgcn_wave_barrier();
-        constexpr int LPR = 8 * SP;  // lanes per staged row
+        constexpr int LPR = 8 * SP;    // lanes per staged row
         constexpr int RPI = 64 / LPR;  // rows per instruction
         const int rr = lane / LPR, cc = 4 * (lane % LPR);
-        const int c0 = n0 + wn + 32 * j, r0 = m0 + wm + 32 * (i - (SP - 1));
+        const int c0 = n0 + wn + 32 * j, r0 = m0 + wm + 32 * i0;
+        // on a diagonal tile: whether this lane's source block was computed by this wave
+        const bool src = !decltype(DG)::value || ((mask >> ((i0 + cc / 32) * TN + j)) & 1);
 #pragma unroll
         for (int t = 0; t < 32 / RPI; ++t) {
           const int row = RPI * t + rr;
-          tile.write4t(c0 + row, r0 + cc, *reinterpret_cast<const floatx4*>(stage + row * LDT + cc));
+          const floatx4 v = *reinterpret_cast<const floatx4*>(stage + row * LDT + cc);
+          if constexpr (!decltype(DG)::value) {
+            tile.write4t(c0 + row, r0 + cc, v);
+          } else if (src) {
+            if (r0 + cc + 3 < c0 + row) {
+              tile.write4t(c0 + row, r0 + cc, v);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (r0 + cc + e < c0 + row) tile.write(c0 + row, r0 + cc + e, v[e]);
+            }
+          }
         }
         __builtin_amdgcn_wave_barrier();
       }
@@ -294,13 +319,15 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
   // groups prefetched together: at most the epilogue's wish, the caller's register budget and the groups there are
   constexpr int K0 = Tile::kPrefetch < KPRE ? Tile::kPrefetch : KPRE;
   constexpr int K = K0 < TM * TN * 4 ? K0 : TM * TN * 4;
-  auto body = [&](auto&& out) __attribute__((always_inline)) {
+  auto body = [&](auto&& out, auto&& after) __attribute__((always_inline)) {
     if constexpr (K == 0) {
       static_for<TM * TN * 4>([&](auto G) __attribute__((always_inline)) {
-        if (!computed(G)) return;
-        int r, c;
-        rc(G, r, c);
-        out(G, tile.value4(r, c, acc4(G)));
+        if (computed(G)) {
+          int r, c;
+          rc(G, r, c);
+          out(G, tile.value4(r, c, acc4(G)));
+        }
+        after(G);
       });
     } else {
       // The epilogue's own inputs are requested a chunk of K groups at a time,
@@ -325,21 +352,28 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
         static_for<K>([&](auto G) __attribute__((always_inline)) {
           constexpr int g = decltype(C)::value * K + decltype(G)::value;
           const std::integral_constant<int, g> gi{};
-          if (!computed(gi)) return;
-          int r, c;
-          rc(gi, r, c);
-          out(gi, tile.value4p(r, c, acc4(gi), pre[decltype(C)::value & 1][decltype(G)::value]));
+          if (computed(gi)) {
+            int r, c;
+            rc(gi, r, c);
+            out(gi, tile.value4p(r, c, acc4(gi), pre[decltype(C)::value & 1][decltype(G)::value]));
+          }
+          after(gi);
         });
       });
     }
   };
   if constexpr (SP > 0) {
-    if (!diag) {
-      body(emit_staged);
-      return;
-    }
+    auto staged = [&](auto DG) __attribute__((always_inline)) {
+      body([&](auto G, const auto& o) __attribute__((always_inline)) { emit_staged(DG, G, o); },
+           [&](auto G) __attribute__((always_inline)) { flush(DG, G); });
+    };
+    if (diag)
+      staged(std::true_type{});
+    else
+      staged(std::false_type{});
+  } else {
+    body(emit, [](auto) {});
   }
-  body(emit);
 }
 
 // Workgroup lid -> (job, item, tile row tm, tile column tn), item-major: the
