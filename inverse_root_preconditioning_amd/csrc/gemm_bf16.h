@@ -466,8 +466,10 @@ __device__ __forceinline__ void h16_wave_role8(bool dtile, int wave, int& wm, in
 
 // WAVES = 16: 4 x 4 waves of 64 x 64 (128 VGPRs each).  WAVES = 8: 4 x 2 waves
 // of 64 x 128 (256 VGPRs each), for epilogues that want registers to load
-// ahead; on a diagonal tile of a symmetric product its waves wholly below
-// the diagonal idle and the others compute their whole block.
+// ahead.  On a diagonal tile of a symmetric product the 8-wave layout places
+// its waves by h16_wave_role8 for the register-direct symmetric epilogue;
+// for the LDS-staged one (plain 4 x 2 order) the waves wholly below the
+// diagonal idle and the others compute their whole block.
 template <class Epi, int FMT, bool SYM, int WAVES>
 __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16Launch<Epi> P) {
   static_assert(WAVES == 16 || WAVES == 8, "wave layouts");

@@ -211,12 +211,13 @@ __device__ __forceinline__ float sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN
   return part;
 }
 
-// Epilogue of a symmetric product without LDS (kDirect epilogues).  For each
-// group of four accumulators a lane holds rows r..r+3 of one column c: it
-// writes them there (on a diagonal tile only on and above the diagonal) and
-// writes the mirrored entries, columns r..r+3 of row c, with one vector
-// store (on a diagonal tile only those strictly below the diagonal).  Only
-// the 32 x 32 blocks (i, j) with bit i TN + j of `mask` set are written.
+// Epilogue of a symmetric product from registers (kDirect epilogues).  For
+// each group of four accumulators a lane holds rows r..r+3 of one column c:
+// it writes them there (on a diagonal tile only on and above the diagonal)
+// and, with SP = 0, writes the mirrored entries, columns r..r+3 of row c,
+// with one vector store (on a diagonal tile only those strictly below the
+// diagonal).  Only the 32 x 32 blocks (i, j) with bit i TN + j of `mask`
+// set are written.
 // KPRE bounds how many groups' epilogue inputs are loaded ahead (registers).
 //
 // SP > 0: the mirrored half goes through `stage`, this wave's 32 x (32 SP + 4)
