@@ -519,6 +519,67 @@ __global__ void __launch_bounds__(256) ew_kernel(const EwArgs P) {
   }
 }
 
+// Start of the bf16-input Chebyshev evaluation with its 16-bit operands, per
+// 64 x 64 tile of a factor: A_s = a x + b I (a = 1/c, b = eps/c, both 0 for a
+// degenerate factor), b_d = c_d I and b_{d-1} = c_{d-1} I + 2 c_d (2 A_s - I)
+// as EW_CHEBY_START forms them, written in fp32, together with the bf16 copy
+// of b_{d-1} and the transposed bf16 copy of A_s (the NT operand of the
+// Clenshaw products); A_s itself is not stored.  B is a multiple of 64.
+struct Cheby16StartArgs {
+  const float* x;            // factors [nf][B][B]
+  const shampoo_scale* sc;   // c and eps per factor
+  const int32_t* status;
+  float* bd;                 // b_d
+  float* bd1;                // b_{d-1}
+  uint16_t* bd1_16;          // bf16(b_{d-1})
+  uint16_t* as_t16;          // bf16(A_s) transposed
+  float cd, cd1;             // c_d, c_{d-1}
+  int B;
+  int tiles;                 // (B / 64)^2
+};
+
+__global__ void __launch_bounds__(256) cheby16_start_kernel(const Cheby16StartArgs P) {
+  __shared__ float t[64][65];
+  const int64_t f = blockIdx.x / P.tiles;
+  const int tt = blockIdx.x - (int)(f * P.tiles);
+  const int per = P.B / 64;
+  const int r0 = (tt / per) * 64, c0 = (tt % per) * 64;
+  const float c = safe_c(P.sc, P.status, f);
+  float a = 1.f / c, b = P.sc[f].eps / c;
+  if (P.status != nullptr && degenerate(P.status[f])) {
+    a = 0.f;
+    b = 0.f;
+  }
+  const int64_t base = f * (int64_t)P.B * P.B;
+  const int tid = threadIdx.x;
+  const int cr = tid >> 4, cc = (tid & 15) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = r0 + cr + 16 * i, col = c0 + cc;
+    const int64_t idx = base + (int64_t)row * P.B + col;
+    const floatx4 xv = ldg(reinterpret_cast<const floatx4*>(P.x + idx));
+    floatx4 o1, o2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = (row == col + e) ? 1.f : 0.f;
+      const float y = a * xv[e] + b * d;
+      o1[e] = P.cd * d;
+      o2[e] = P.cd1 * d + 2.f * P.cd * (2.f * y - d);
+      t[cr + 16 * i][cc + e] = y;
+    }
+    stg(reinterpret_cast<floatx4*>(P.bd + idx), o1);
+    stg(reinterpret_cast<floatx4*>(P.bd1 + idx), o2);
+    stg4_h16(P.bd1_16 + idx, o2, H16_BF16);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lr = cr + 16 * i;
+    const floatx4 y = {t[cc][lr], t[cc + 1][lr], t[cc + 2][lr], t[cc + 3][lr]};
+    stg4_h16(P.as_t16 + base + (int64_t)(c0 + lr) * P.B + r0 + cc, y, H16_BF16);
+  }
+}
+
 // resid[f][col] = sqrt(sum of partials[f][:count]); NONFINITE if not finite.
 __global__ void __launch_bounds__(64) resid_kernel(const float* __restrict__ partials, int count,
                                                   float* __restrict__ resid, int ncols, int col,

@@ -881,18 +881,34 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
     a.extra = 1.f;
     return run_ew<EW_CHEBY_LINEAR>(a, nf, st);
   }
-  a.out0 = ws->as;
-  a.out1 = ws->b[0];  // b_d
-  a.out2 = ws->b[1];  // b_{d-1}
-  a.c0 = (float)c[degree];
-  a.c1 = (float)c[degree - 1];
-  SHP_TRY(run_ew<EW_CHEBY_START>(a, nf, st));
   const bool bf = (prec == SHAMPOO_BF16_IN);
   int i2 = 0, i1 = 1, i0 = 2;  // ring slots of b_{j+2}, b_{j+1}, b_j
   int s1 = 0;                  // bf16 slot holding b_{j+1}
   if (bf) {
-    SHP_TRY(bf16_cast(ws->as, ws->as_t16, nf, B, true, st));
-    SHP_TRY(bf16_cast(ws->b[i1], ws->b16[s1], nf, B, false, st));
+    // b_d, b_{d-1} and the 16-bit operands in one pass (A_s is only needed as bf16)
+    Cheby16StartArgs s;
+    s.x = F;
+    s.sc = sc;
+    s.status = status;
+    s.bd = ws->b[i2];
+    s.bd1 = ws->b[i1];
+    s.bd1_16 = ws->b16[s1];
+    s.as_t16 = ws->as_t16;
+    s.cd = (float)c[degree];
+    s.cd1 = (float)c[degree - 1];
+    s.B = B;
+    s.tiles = (B / 64) * (B / 64);
+    const uint64_t grid = (uint64_t)nf * s.tiles;
+    if (grid > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
+    if (grid > 0) hipLaunchKernelGGL(cheby16_start_kernel, dim3((uint32_t)grid), dim3(256), 0, st, s);
+    SHP_TRY(check_launch());
+  } else {
+    a.out0 = ws->as;
+    a.out1 = ws->b[i2];  // b_d
+    a.out2 = ws->b[i1];  // b_{d-1}
+    a.c0 = (float)c[degree];
+    a.c1 = (float)c[degree - 1];
+    SHP_TRY(run_ew<EW_CHEBY_START>(a, nf, st));
   }
   for (int j = degree - 2; j >= 0; --j) {
     EpiClenshaw::Job e;
