@@ -101,6 +101,7 @@ struct PiArgs {
   const shampoo_scale* sc; // eps
   int B;
   int npanels;
+  int npanels_in;          // panels of norm_in (those of the previous step)
   uint32_t total;          // nf * npanels
   int last;
 };
@@ -131,7 +132,7 @@ __global__ void __launch_bounds__(256, 2) pi_step_kernel(const PiArgs P) {
         s = 1.f;
       } else {
         float n2 = 0.f;
-        for (int p = 0; p < P.npanels; ++p) n2 += P.norm_in[(f * P.npanels + p) * kPiCols + j];
+        for (int p = 0; p < P.npanels_in; ++p) n2 += P.norm_in[(f * P.npanels_in + p) * kPiCols + j];
         s = (n2 > 0.f) ? 1.f / sqrtf(n2) : ((n2 == 0.f) ? 0.f : n2);  // NaN propagates
       }
     }
@@ -276,7 +277,7 @@ __global__ void __launch_bounds__(256, 2) pi_step_dma_kernel(const PiArgs P) {
         s = 1.f;
       } else {
         float n2 = 0.f;
-        for (int p = 0; p < P.npanels; ++p) n2 += P.norm_in[(f * P.npanels + p) * kPiCols + j];
+        for (int p = 0; p < P.npanels_in; ++p) n2 += P.norm_in[(f * P.npanels_in + p) * kPiCols + j];
         s = (n2 > 0.f) ? 1.f / sqrtf(n2) : ((n2 == 0.f) ? 0.f : n2);  // NaN propagates
       }
     }
@@ -374,6 +375,136 @@ __global__ void __launch_bounds__(256, 2) pi_step_dma_kernel(const PiArgs P) {
     for (int b = 0; b < 4; ++b) {
       n += colsum[b * kPiCols + c];
       q += colsum[(4 + b) * kPiCols + c];
+    }
+    P.norm_out[o] = n;
+    if (P.last) P.rq_out[o] = q;
+  }
+}
+
+// The same step for 256-column panels when V has 32 columns per row and B is
+// a multiple of 256, reading F by columns: F is symmetric (the factors are
+// formed as symmetric products), so W = F V = F^T V and a stage can take 16
+// whole rows k of the panel's 256 columns (1 KB each), the access shape HBM
+// serves fastest, instead of 128-byte pieces of many rows.  8 waves, each
+// 32 columns of the panel (rows of W); k staged 16 deep through a ring of
+// four stages, three ahead, one barrier per stage.  Rows 2t and 2t + 1 of F
+// sit 1152 bytes apart in LDS, so that the two k rows one MFMA reads (lanes
+// 0..31 and 32..63) fall on different banks; V is [k][32].
+__global__ void __launch_bounds__(512, 2) pi_step_col_kernel(const PiArgs P) {
+  constexpr int PANEL = 256, BK = 16, NW = 8, NB = 4;
+  // F row r at r PANEL + ((r + 1) / 2) 32 floats: rows 2t and 2t + 1 are 128 bytes off modulo 256
+  auto frow = [](int r) { return r * PANEL + ((r + 1) >> 1) * 32; };
+  constexpr int kF = (BK - 1) * PANEL + (BK / 2) * 32 + PANEL, kV = BK * kPiCols, kStage = kF + kV;  // floats
+  constexpr int NL = 3;                                // loads per thread and stage
+  constexpr int kWaitAhead = (NL * (NB - 2)) | (7 << 4);
+  // One LDS object (see gemm_f32_big_kernel): the ring, then s_col and the column sums.
+  __shared__ __attribute__((aligned(16))) float lds[NB * kStage + kPiCols + 2 * NW * kPiCols];
+  float* const s_col = lds + NB * kStage;
+  float* const colsum = s_col + kPiCols;  // [2 (W², ṽ·w)][8 row blocks][32]
+  const uint32_t lid = xcd_remap(blockIdx.x, P.total);
+  const int64_t f = lid / P.npanels;
+  const int panel = lid - (uint32_t)f * P.npanels;
+  const int m0 = panel * PANEL;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid < kPiCols) {
+    const int j = tid;
+    float s = 0.f;
+    if (j < P.r) {
+      if (P.norm_in == nullptr) {
+        s = 1.f;
+      } else {
+        float n2 = 0.f;
+        for (int p = 0; p < P.npanels_in; ++p) n2 += P.norm_in[(f * P.npanels_in + p) * kPiCols + j];
+        s = (n2 > 0.f) ? 1.f / sqrtf(n2) : ((n2 == 0.f) ? 0.f : n2);  // NaN propagates
+      }
+    }
+    s_col[j] = s;
+  }
+  const int B = P.B;
+  const float* Fp = P.F + f * (int64_t)B * B;
+  const float* Vp = P.vin + f * (int64_t)B * kPiCols;
+  // F: wave instruction it of wave w loads row k = 2 w + it of the stage, its 256 columns;
+  // V: 4-byte pieces, wave w loads rows 2 w and 2 w + 1 (lanes 0..31 and 32..63)
+  const float* srcF[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) srcF[it] = Fp + (int64_t)(2 * wave + it) * B + m0 + 4 * lane;
+  const float* srcV = Vp + (int64_t)(2 * wave + (lane >> 5)) * kPiCols + (lane & 31);
+  const int nstages = B / BK;
+  auto issue = [&](float* __restrict__ buf, int s) __attribute__((always_inline)) {
+    const int64_t k0 = min(s, nstages - 1) * BK;  // past the end: the last stage again, never read
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcF[it] + k0 * B),
+                                       (__attribute__((address_space(3))) void*)(buf + frow(2 * wave + it)),
+                                       16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcV + k0 * kPiCols),
+                                     (__attribute__((address_space(3))) void*)(buf + kF + wave * 64), 4, 0, 0);
+  };
+  floatx16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < NB - 1; ++p) issue(lds + p * kStage, p);
+  __builtin_amdgcn_s_waitcnt(kWaitAhead);
+  __builtin_amdgcn_s_barrier();
+  const int h = lane >> 5, mcol = wave * 32 + (lane & 31);
+  auto step = [&](const float* __restrict__ rd, float* __restrict__ wr, int s) __attribute__((always_inline)) {
+    issue(wr, s + NB - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    float fa[BK / 2], fv[BK / 2];
+#pragma unroll
+    for (int t = 0; t < BK / 2; ++t) {
+      fa[t] = rd[frow(2 * t + h) + mcol];                    // F[k][m] = F[m][k]
+      fv[t] = rd[kF + (2 * t + h) * kPiCols + (lane & 31)];  // V[k][j]
+    }
+#pragma unroll
+    for (int t = 0; t < BK / 2; ++t) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[t], fv[t], acc, 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitAhead);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  int s = 0;
+  for (; s + NB <= nstages; s += NB) {
+    step(lds, lds + 3 * kStage, s);
+    step(lds + kStage, lds, s + 1);
+    step(lds + 2 * kStage, lds + kStage, s + 2);
+    step(lds + 3 * kStage, lds + 2 * kStage, s + 3);
+  }
+  if (s < nstages) step(lds, lds + 3 * kStage, s);
+  if (s + 1 < nstages) step(lds + kStage, lds, s + 1);
+  if (s + 2 < nstages) step(lds + 2 * kStage, lds + kStage, s + 2);
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4));  // the loads issued past the end
+
+  const int j = lane & 31;
+  const float sj = s_col[j];
+  const float eps = P.sc[f].eps;
+  float nsum = 0.f, rsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int row = m0 + wave * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+    const float v = (j < P.r) ? ldg(Vp + (int64_t)row * kPiCols + j) * sj : 0.f;
+    const float w = acc[e] * sj + eps * v;
+    if (!P.last) stg(P.wout + (f * B + row) * kPiCols + j, w);
+    nsum += w * w;
+    rsum += v * w;
+  }
+  nsum += __shfl_xor(nsum, 32, kWave);
+  rsum += __shfl_xor(rsum, 32, kWave);
+  if (lane < 32) {
+    colsum[wave * kPiCols + j] = nsum;
+    colsum[(NW + wave) * kPiCols + j] = rsum;
+  }
+  __syncthreads();
+  if (tid < kPiCols) {
+    const int c = tid;
+    const int64_t o = (f * P.npanels + panel) * kPiCols + c;
+    float n = 0.f, q = 0.f;
+#pragma unroll
+    for (int b = 0; b < NW; ++b) {
+      n += colsum[b * kPiCols + c];
+      q += colsum[(NW + b) * kPiCols + c];
     }
     P.norm_out[o] = n;
     if (P.last) P.rq_out[o] = q;

@@ -1073,8 +1073,6 @@ int shampoo_scale_power(const float* factors, int64_t nfactors, int B, float eps
   P.F = factors;
   P.sc = scale_out;
   P.B = B;
-  P.npanels = B / panel;
-  P.total = (uint32_t)(nfactors * P.npanels);
   P.rq_out = w.rq;
   for (int t = 0; t <= steps; ++t) {
     P.vin = (t == 0) ? v0 : w.w[(t - 1) & 1];
@@ -1084,7 +1082,15 @@ int shampoo_scale_power(const float* factors, int64_t nfactors, int B, float eps
     P.norm_in = (t == 0) ? nullptr : w.norm[(t - 1) & 1];
     P.norm_out = w.norm[t & 1];
     P.last = (t == steps) ? 1 : 0;
-    if (panel == 128 && P.ldv == kPiCols)
+    // after the first step (V then has 32 columns per row): 256-column panels
+    // read by columns when B allows, else the row-panel kernels
+    const bool col = (B % 256 == 0) && P.ldv == kPiCols;
+    P.npanels_in = P.npanels;  // the previous step's panels (unused on the first)
+    P.npanels = col ? B / 256 : B / panel;
+    P.total = (uint32_t)(nfactors * P.npanels);
+    if (col)
+      hipLaunchKernelGGL(pi_step_col_kernel, dim3(P.total), dim3(512), 0, stream, P);
+    else if (panel == 128 && P.ldv == kPiCols)
       hipLaunchKernelGGL(pi_step_dma_kernel, dim3(P.total), dim3(256), 0, stream, P);
     else if (panel == 128)
       hipLaunchKernelGGL(pi_step_kernel<128>, dim3(P.total), dim3(256), 0, stream, P);

@@ -101,8 +101,10 @@ def test_accumulate_bf16_input():
 # scale
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("B,r", [(64, 32), (192, 32), (256, 7)])
+@pytest.mark.parametrize("B,r", [(64, 32), (192, 32), (256, 7), (768, 32), (1024, 20)])
 def test_scale_power_matches_oracle(B, r):
+    """B = 64 and 192 run the 64-row panel step, the others the 256-column
+    panels read by columns after the first step (3 and 4 panels per factor)."""
     nf = 6
     F = W.spd_factors(10 + B, nf, B, cond=1e4) * np.float32(3.0)
     V0 = W.start_vectors(9, nf, B, r)
