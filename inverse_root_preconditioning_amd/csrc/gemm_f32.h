@@ -1017,8 +1017,9 @@ struct EpiClenshaw {
     uint16_t* out16;     // optional 16-bit copy of b (operand of the next product)
     int fmt16;
     const float* b1;
-    const float* b2;
+    const float* b2;     // null: b2 = c2 I, formed here (the loads for it then read b1's lines)
     float cj;
+    float c2;
     int final;
     const shampoo_scale* scale;
     const int32_t* status;
@@ -1034,8 +1035,8 @@ struct EpiClenshaw {
     int fmt;
     const float* b1;
     const float* b2;
-    float cj, mult, k1, k2;
-    bool ident, is_final;
+    float cj, mult, k1, k2, c2;
+    bool ident, is_final, b2_diag;
     int B;
     __device__ __forceinline__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
       const int64_t off = item * (int64_t)B_ * B_;
@@ -1043,7 +1044,9 @@ struct EpiClenshaw {
       obf = j.out16 ? j.out16 + off : nullptr;
       fmt = j.fmt16;
       b1 = j.b1 + off;
-      b2 = j.b2 + off;
+      b2_diag = j.b2 == nullptr;
+      b2 = b2_diag ? b1 : j.b2 + off;
+      c2 = j.c2;
       cj = j.cj;
       is_final = j.final != 0;
       if (j.final) {
@@ -1061,7 +1064,8 @@ struct EpiClenshaw {
     __device__ __forceinline__ float value(int row, int col, float v) const {
       const int64_t idx = (int64_t)row * B + col;
       const float d = (row == col) ? cj : 0.f;
-      float o = mult * (d + k1 * v - k2 * ldg(b1 + idx) - ldg(b2 + idx));
+      const float x2 = b2_diag ? ((row == col) ? c2 : 0.f) : ldg(b2 + idx);
+      float o = mult * (d + k1 * v - k2 * ldg(b1 + idx) - x2);
       if (ident) o = (row == col) ? 1.f : 0.f;
       return o;
     }
@@ -1081,7 +1085,8 @@ struct EpiClenshaw {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool dg = (r + e == c);
-        o[e] = ident ? (dg ? 1.f : 0.f) : mult * ((dg ? cj : 0.f) + k1 * v[e] - k2 * p.x1[e] - p.x2[e]);
+        const float x2 = b2_diag ? (dg ? c2 : 0.f) : p.x2[e];
+        o[e] = ident ? (dg ? 1.f : 0.f) : mult * ((dg ? cj : 0.f) + k1 * v[e] - k2 * p.x1[e] - x2);
       }
       return o;
     }

@@ -652,15 +652,16 @@ __global__ void __launch_bounds__(256) ew_kernel(const EwArgs P) {
 
 // Start of the bf16-input Chebyshev evaluation with its 16-bit operands, per
 // 64 x 64 tile of a factor: A_s = a x + b I (a = 1/c, b = eps/c, both 0 for a
-// degenerate factor), b_d = c_d I and b_{d-1} = c_{d-1} I + 2 c_d (2 A_s - I)
-// as EW_CHEBY_START forms them, written in fp32, together with the bf16 copy
-// of b_{d-1} and the transposed bf16 copy of A_s (the NT operand of the
-// Clenshaw products); A_s itself is not stored.  B is a multiple of 64.
+// degenerate factor) and b_{d-1} = c_{d-1} I + 2 c_d (2 A_s - I) as
+// EW_CHEBY_START forms it, written in fp32, together with the bf16 copy of
+// b_{d-1} and the transposed bf16 copy of A_s (the NT operand of the Clenshaw
+// products); A_s itself is not stored, nor b_d = c_d I unless `bd` is given
+// (the first Clenshaw step forms it).  B is a multiple of 64.
 struct Cheby16StartArgs {
   const float* x;            // factors [nf][B][B]
   const shampoo_scale* sc;   // c and eps per factor
   const int32_t* status;
-  float* bd;                 // b_d
+  float* bd;                 // b_d (optional)
   float* bd1;                // b_{d-1}
   uint16_t* bd1_16;          // bf16(b_{d-1})
   uint16_t* as_t16;          // bf16(A_s) transposed
@@ -698,7 +699,7 @@ __global__ void __launch_bounds__(256) cheby16_start_kernel(const Cheby16StartAr
       o2[e] = P.cd1 * d + 2.f * P.cd * (2.f * y - d);
       t[cr + 16 * i][cc + e] = y;
     }
-    stg(reinterpret_cast<floatx4*>(P.bd + idx), o1);
+    if (P.bd) stg(reinterpret_cast<floatx4*>(P.bd + idx), o1);
     stg(reinterpret_cast<floatx4*>(P.bd1 + idx), o2);
     stg4_h16(P.bd1_16 + idx, o2, H16_BF16);
   }

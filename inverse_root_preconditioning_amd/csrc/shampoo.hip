@@ -890,7 +890,7 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
     s.x = F;
     s.sc = sc;
     s.status = status;
-    s.bd = ws->b[i2];
+    s.bd = nullptr;  // b_d = c_d I: the first Clenshaw step forms it
     s.bd1 = ws->b[i1];
     s.bd1_16 = ws->b16[s1];
     s.as_t16 = ws->as_t16;
@@ -916,7 +916,8 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
     e.out16 = (bf && j > 0) ? ws->b16[s1 ^ 1] : nullptr;
     e.fmt16 = H16_BF16;
     e.b1 = ws->b[i1];
-    e.b2 = ws->b[i2];
+    e.b2 = (bf && j == degree - 2) ? nullptr : ws->b[i2];  // bf16 path: b_d not stored
+    e.c2 = (float)c[degree];
     e.cj = (float)c[j];
     e.final = (j == 0) ? 1 : 0;
     e.scale = sc;
