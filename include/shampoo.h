@@ -165,7 +165,12 @@ int shampoo_accumulate(const shampoo_block* g_blocks, int64_t nblocks, int B,
  * [DASH] "Building blocks" (multi-power-iteration; Frobenius versus spectral
  * scaling) and "Step-by-step", scaling each block.
  *
- *   factors    device float[nfactors][B][B] (not modified); A = F + eps I
+ *   factors    device float[nfactors][B][B] (not modified); A = F + eps I.
+ *              F is taken to be symmetric, as a factor formed by
+ *              shampoo_accumulate is: when B is a multiple of 256, rounds
+ *              after the first form W = A^T V (reading F by columns).  For
+ *              an F that is not symmetric that is the same iteration on A^T,
+ *              which has A's eigenvalues.
  *   eps_rel    eps = eps_rel * tr(F) / B (>= 0)
  *   mode       SHAMPOO_SCALE_POWER: r start vectors v0, `steps` rounds of
  *                W = A V, columns normalised; then q_j = v_j^T A v_j,
