@@ -256,7 +256,8 @@ def main(argv=None):
         half = base_variant == capi.CN_F16
         peak = PEAK_BF16_MFMA if half else PEAK_F32_MFMA
         h16_cn = "gemm_h16_big_kernel<EpiCnM, fp16, 8 waves>" if B % 256 == 0 else "gemm_h16_nt_kernel<EpiCnM, fp16>"
-        kname = (h16_cn if half else "gemm_f32_kernel<EpiCnM>") + \
+        f32_cn = "gemm_f32_big_kernel<EpiCnM>" if B % 256 == 0 else "gemm_f32_kernel<EpiCnM>"
+        kname = (h16_cn if half else f32_cn) + \
             " (coupled Newton C^p M, one full product per factor)"
     elif cfg.solver == "newton":
         family, per_step = capi.TIME_NDB_PAIR, 2 * (cfg.iters - 2)

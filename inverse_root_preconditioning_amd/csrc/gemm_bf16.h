@@ -68,70 +68,6 @@ __device__ __forceinline__ floatx16 mfma_h16(const u32x4& a, const u32x4& b, con
   }
 }
 
-// Epilogue through LDS for workgroups with many accumulators: in each of PH
-// phases the waves whose rows fall in it stage their raw accumulators, then
-// all NT threads apply the epilogue in row-major order (consecutive threads,
-// consecutive columns), so no accumulator register is live while the
-// epilogue's own loads are in flight.  For a symmetric product (`sym`) the
-// value formed at each computed position is written there (on a diagonal
-// tile only on and above the diagonal), kept in LDS, and written mirrored
-// through a transposed pass, and the reduction is weighted as in
-// sym_epilogue.  `lds` needs (BM / PH) x (BN + 1) floats and must be free.
-// Returns this thread's share of the tile's reduction.
-template <int TM, int TN, int BM, int BN, int NT, int PH, class Epi>
-__device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, floatx16 (&acc)[TM][TN], float* lds,
-                                                 int m0, int n0, int wm, int wn, int lane, bool sym, bool diag) {
-  constexpr int LD = BN + 1, RH = BM / PH;
-  static_assert(RH % (32 * TM) == 0, "a wave's rows must fall in one phase");
-  float part = 0.f;
-#pragma unroll
-  for (int h = 0; h < PH; ++h) {
-    if (PH == 1 || wm / RH == h) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int rl = wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            const int cl = wn + 32 * j + (lane & 31);
-            lds[(rl - h * RH) * LD + cl] = acc[i][j][e];
-          }
-    }
-    __syncthreads();
-    const int r0 = m0 + h * RH;
-    if constexpr (Epi::kSym) {
-      if (sym) {
-        for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
-          const int b = idx / BN, a = idx - (idx / BN) * BN;
-          if constexpr (Epi::kReduce) {  // weights as in sym_epilogue
-            const int rg = r0 + b, cg = n0 + a;
-            const float w = !diag ? 1.f : (rg < cg ? 2.f : (rg == cg ? 1.f : 0.f));
-            part += w * tile.contrib(rg, cg, lds[b * LD + a]);
-          }
-          const float o = tile.value(r0 + b, n0 + a, lds[b * LD + a]);
-          if (!diag || r0 + b <= n0 + a) tile.write(r0 + b, n0 + a, o);
-          lds[b * LD + a] = o;
-        }
-        __syncthreads();
-        // o[b][a] goes to (n0 + a, r0 + b); on a diagonal tile only from above the diagonal.
-        for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
-          const int a = idx / RH, b = idx - (idx / RH) * RH;
-          if (!diag || n0 + a > r0 + b) tile.write(n0 + a, r0 + b, lds[b * LD + a]);
-        }
-        if (h + 1 < PH) __syncthreads();
-        continue;
-      }
-    }
-    for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
-      const int b = idx / BN, a = idx - (idx / BN) * BN;
-      part += tile.store(r0 + b, n0 + a, lds[b * LD + a]);
-    }
-    if (h + 1 < PH) __syncthreads();
-  }
-  return part;
-}
-
 // Workgroup shapes of the 16-bit product.  The LDS traffic per MFMA falls
 // with the wave tile: 64 x 64 wave tiles read 1 KB of fragments per 32 x 32 x 16
 // MFMA, 64 x 128 ones 0.75 KB, and the 256 x 256 workgroup tile halves the

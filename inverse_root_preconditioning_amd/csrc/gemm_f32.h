@@ -211,6 +211,70 @@ __device__ __forceinline__ float sym_epilogue(Tile& tile, floatx16 (&acc)[TM][TN
   return part;
 }
 
+// Epilogue through LDS for workgroups with many accumulators: in each of PH
+// phases the waves whose rows fall in it stage their raw accumulators, then
+// all NT threads apply the epilogue in row-major order (consecutive threads,
+// consecutive columns), so no accumulator register is live while the
+// epilogue's own loads are in flight.  For a symmetric product (`sym`) the
+// value formed at each computed position is written there (on a diagonal
+// tile only on and above the diagonal), kept in LDS, and written mirrored
+// through a transposed pass, and the reduction is weighted as in
+// sym_epilogue.  `lds` needs (BM / PH) x (BN + 1) floats and must be free.
+// Returns this thread's share of the tile's reduction.
+template <int TM, int TN, int BM, int BN, int NT, int PH, class Epi>
+__device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, floatx16 (&acc)[TM][TN], float* lds,
+                                                 int m0, int n0, int wm, int wn, int lane, bool sym, bool diag) {
+  constexpr int LD = BN + 1, RH = BM / PH;
+  static_assert(RH % (32 * TM) == 0, "a wave's rows must fall in one phase");
+  float part = 0.f;
+#pragma unroll
+  for (int h = 0; h < PH; ++h) {
+    if (PH == 1 || wm / RH == h) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int rl = wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            const int cl = wn + 32 * j + (lane & 31);
+            lds[(rl - h * RH) * LD + cl] = acc[i][j][e];
+          }
+    }
+    __syncthreads();
+    const int r0 = m0 + h * RH;
+    if constexpr (Epi::kSym) {
+      if (sym) {
+        for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
+          const int b = idx / BN, a = idx - (idx / BN) * BN;
+          if constexpr (Epi::kReduce) {  // weights as in sym_epilogue
+            const int rg = r0 + b, cg = n0 + a;
+            const float w = !diag ? 1.f : (rg < cg ? 2.f : (rg == cg ? 1.f : 0.f));
+            part += w * tile.contrib(rg, cg, lds[b * LD + a]);
+          }
+          const float o = tile.value(r0 + b, n0 + a, lds[b * LD + a]);
+          if (!diag || r0 + b <= n0 + a) tile.write(r0 + b, n0 + a, o);
+          lds[b * LD + a] = o;
+        }
+        __syncthreads();
+        // o[b][a] goes to (n0 + a, r0 + b); on a diagonal tile only from above the diagonal.
+        for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
+          const int a = idx / RH, b = idx - (idx / RH) * RH;
+          if (!diag || n0 + a > r0 + b) tile.write(n0 + a, r0 + b, lds[b * LD + a]);
+        }
+        if (h + 1 < PH) __syncthreads();
+        continue;
+      }
+    }
+    for (int idx = threadIdx.x; idx < RH * BN; idx += NT) {
+      const int b = idx / BN, a = idx - (idx / BN) * BN;
+      part += tile.store(r0 + b, n0 + a, lds[b * LD + a]);
+    }
+    if (h + 1 < PH) __syncthreads();
+  }
+  return part;
+}
+
 // Epilogue of a symmetric product from registers (kDirect epilogues).  For
 // each group of four accumulators a lane holds rows r..r+3 of one column c:
 // it writes them there (on a diagonal tile only on and above the diagonal)
@@ -770,9 +834,21 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __syncthreads();
 
-  // mirrored half of symmetric tiles staged per 32 x 32 block (16 waves x 4.5 KB of the stage buffers)
-  static_assert(NT / kWave * 32 * 36 + NT / kWave <= 3 * kStage, "staging and reduction fit the buffers");
-  gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM, 1, 1>(P, job, item, tm, tn, acc, lds, red, m0, n0, wm, wn, lane, mask);
+  if constexpr (Epi::kBigStaged && !SYM) {
+    // full product with its epilogue through LDS (accumulators staged in PH phases)
+    typename Epi::Tile tile(*(job == 0 ? &P.e[0] : &P.e[1]), item, P.B);
+    const float part =
+        staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, lds, m0, n0, wm, wn, lane, false, false);
+    if constexpr (Epi::kReduce) {
+      const float tot = block_sum<NT>(part, red);
+      if (threadIdx.x == 0) tile.partial(tm * P.tiles_n + tn, tot);
+    }
+  } else {
+    // mirrored half of symmetric tiles staged per 32 x 32 block (16 waves x 4.5 KB of the stage buffers)
+    static_assert(NT / kWave * 32 * 36 + NT / kWave <= 3 * kStage, "staging and reduction fit the buffers");
+    gemm_epilogue<TM, TN, BM, BN, NT, PH, SYM, 1, 1>(P, job, item, tm, tn, acc, lds, red, m0, n0, wm, wn, lane,
+                                                     mask);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -799,6 +875,7 @@ struct EpiStore {
   // gemm_f32_big_kernel fits 128 VGPRs without spilling (symmetric / full);
   // kH16Big*: the same for gemm_h16_big_kernel, where it also has to pay off
   static constexpr bool kBigSym = true, kBigFull = false;
+  static constexpr bool kBigStaged = false;  // full products of the large kernel: register-direct epilogue
   static constexpr bool kH16BigSym = true, kH16BigFull = false;
   static constexpr int kH16BigWaves = 16;
   struct Job {
@@ -869,6 +946,7 @@ struct EpiPair : EpiStore {};
 // Output through a block descriptor: only rows x cols of the block is written.
 struct EpiStoreDesc {
   static constexpr bool kBigSym = false, kBigFull = true;
+  static constexpr bool kBigStaged = false;
   static constexpr bool kH16BigSym = false, kH16BigFull = true;
   static constexpr int kH16BigWaves = 16;
   static constexpr bool kSym = false;
@@ -904,6 +982,7 @@ struct EpiNdbE {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = false;
   static constexpr bool kBigSym = false, kBigFull = true;
+  static constexpr bool kBigStaged = false;
   static constexpr bool kH16BigSym = false, kH16BigFull = false;
   static constexpr int kH16BigWaves = 16;
   static constexpr bool kReduce = true;
@@ -942,7 +1021,10 @@ struct EpiNdbE {
 struct EpiCnM {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = false;
-  static constexpr bool kBigSym = false, kBigFull = false;
+  // full products on the large fp32 kernel with the epilogue through LDS (in
+  // registers it spills there); symmetric ones on the 128-wide kernel
+  static constexpr bool kBigSym = false, kBigFull = true;
+  static constexpr bool kBigStaged = true;
   // 16-bit: the 8-wave layout with its epilogue through LDS
   static constexpr bool kH16BigSym = true, kH16BigFull = true;
   static constexpr int kH16BigWaves = 8;
@@ -1008,6 +1090,7 @@ struct EpiClenshaw {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = true;
   static constexpr bool kBigSym = true, kBigFull = false;
+  static constexpr bool kBigStaged = false;
   // 16-bit: the 8-wave layout, whose registers let the epilogue load 4
   // groups of b1/b2 ahead (the 16-wave one, with 1, measured slower)
   static constexpr bool kH16BigSym = true, kH16BigFull = false;

@@ -173,14 +173,15 @@ SPAN_CASES = [("newton", capi.NDB_Z, 6, False), ("newton", capi.NDB, 6, False), 
 
 
 @pytest.mark.parametrize("B,solver,variant,arg,full",
-                         [(B,) + c for B in (512, 768) for c in SPAN_CASES] +
-                         [(1280,) + SPAN_CASES[0], (1280,) + SPAN_CASES[4]])
+                         [(B,) + c for B in (512, 640, 768) for c in SPAN_CASES] +
+                         [(1280,) + SPAN_CASES[0], (1280,) + SPAN_CASES[3], (1280,) + SPAN_CASES[4]])
 def test_fp32_products_span_tiles(B, solver, variant, arg, full):
     """fp32 roots on several output tiles per factor: B = 512 runs the 256 x 256
     direct-to-LDS kernel on 2 x 2 tiles (3 upper tiles, two of them diagonal),
-    B = 1280 on 5 x 5 (15 upper tiles), B = 768 the 128 x 128 kernel on 6 x 6
-    tiles; symmetric and full products, reductions and epilogues all cross
-    tile boundaries."""
+    B = 768 on 3 x 3 and B = 1280 on 5 x 5 (15 upper tiles; the coupled-Newton
+    C^p M product with its epilogue through LDS), B = 640 the 128 x 128 kernel
+    on 5 x 5 tiles; symmetric and full products, reductions and epilogues all
+    cross tile boundaries."""
     nf = 3
     F = W.spd_factors(70 + B, nf, B, cond=1e3)
     V0 = W.start_vectors(71, nf, B)
