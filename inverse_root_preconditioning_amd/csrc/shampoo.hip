@@ -307,7 +307,8 @@ struct ChebyWs {
 
 size_t cheby_layout(Carver& c, int64_t nf, int B, int prec, ChebyWs* out) {
   ChebyWs w;
-  w.as = c.take<float>(stack_elems(nf, B));
+  // the bf16-input path keeps A_s only as its transposed bf16 copy
+  w.as = (prec == SHAMPOO_BF16_IN) ? nullptr : c.take<float>(stack_elems(nf, B));
   for (int i = 0; i < 3; ++i) w.b[i] = c.take<float>(stack_elems(nf, B));
   w.as_t16 = nullptr;
   w.b16[0] = w.b16[1] = nullptr;
