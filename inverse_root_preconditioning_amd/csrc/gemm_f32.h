@@ -674,16 +674,17 @@ __device__ __forceinline__ int big_swz(int row) { return ((row >> 1) ^ (row >> 2
 // diagonal, all but (1, 0) on it; and waves 2 and 3 (blocks (0, 3) and
 // (1, 2)) hand their block (1, 1) to waves 8 and 9, idle below the diagonal
 // on the SIMDs with less work, so that each SIMD computes 9 of the tile's 36
-// upper 32 x 32 blocks.
-__device__ __forceinline__ void big_wave_role(bool dtile, int wave, int& wm, int& wn, int& mask) {
-  const bool helper = dtile && (wave == 8 || wave == 9);
+// upper 32 x 32 blocks.  Without `share` (epilogues that stage whole wave
+// blocks through LDS) waves 2 and 3 keep their block (1, 1) and 8 and 9 idle.
+__device__ __forceinline__ void big_wave_role(bool dtile, int wave, int& wm, int& wn, int& mask, bool share = true) {
+  const bool helper = share && dtile && (wave == 8 || wave == 9);
   const int place = (int)((kBigPlace >> (4 * (helper ? wave - 6 : wave))) & 15);
   wm = (place >> 2) * 64;
   wn = (place & 3) * 64;
   mask = 0xF;
   if (dtile) {
     mask = wm > wn ? 0 : (wm == wn ? 0xB : 0xF);
-    if (wave == 2 || wave == 3) mask = 0x7;
+    if (share && (wave == 2 || wave == 3)) mask = 0x7;
     if (helper) mask = 0x8;
   }
 }
@@ -711,8 +712,13 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // diagonal blocks shared between waves only with the register-direct symmetric epilogue
+  constexpr bool kShare = [] {
+    if constexpr (Epi::kSym) return Epi::kDirect && !Epi::kReduce;
+    return true;
+  }();
   int wm, wn, mask;
-  big_wave_role(SYM && tm == tn, wave, wm, wn, mask);
+  big_wave_role(SYM && tm == tn, wave, wm, wn, mask, kShare);
 
   // this thread's pieces: A row r, quad q (stored at quad q ^ swz); B row k, columns 4 nq..
   const float* srcA;
@@ -834,14 +840,24 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __syncthreads();
 
-  if constexpr (Epi::kBigStaged && !SYM) {
-    // full product with its epilogue through LDS (accumulators staged in PH phases)
+  // Through LDS (accumulators staged in PH phases): full products of epilogues
+  // that ask for it, and symmetric products with a reduction (their epilogue
+  // spills in registers; waves idle below the diagonal hold zeros, which that
+  // path neither writes nor counts).
+  constexpr bool kStaged = [] {
+    if constexpr (Epi::kSym && SYM) return Epi::kReduce;
+    return Epi::kBigStaged && !SYM;
+  }();
+  if constexpr (kStaged) {
     typename Epi::Tile tile(*(job == 0 ? &P.e[0] : &P.e[1]), item, P.B);
     const float part =
-        staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, lds, m0, n0, wm, wn, lane, false, false);
+        staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, lds, m0, n0, wm, wn, lane, SYM, tm == tn);
     if constexpr (Epi::kReduce) {
       const float tot = block_sum<NT>(part, red);
-      if (threadIdx.x == 0) tile.partial(tm * P.tiles_n + tn, tot);
+      if (threadIdx.x == 0) {
+        tile.partial(tm * P.tiles_n + tn, tot);
+        if (SYM && tm != tn) tile.partial(tn * P.tiles_n + tm, tot);  // the mirrored tile
+      }
     }
   } else {
     // mirrored half of symmetric tiles staged per 32 x 32 block (16 waves x 4.5 KB of the stage buffers)
@@ -981,7 +997,7 @@ struct EpiStoreDesc {
 struct EpiNdbE {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = false;
-  static constexpr bool kBigSym = false, kBigFull = true;
+  static constexpr bool kBigSym = true, kBigFull = true;
   static constexpr bool kBigStaged = false;
   static constexpr bool kH16BigSym = false, kH16BigFull = false;
   static constexpr int kH16BigWaves = 16;

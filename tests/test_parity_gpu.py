@@ -419,14 +419,16 @@ def test_half_width_products_span_tiles(B):
     report("h16_tiles_precondition", B=B, err=err)
 
 
-@pytest.mark.parametrize("variant,iters,tol", [(capi.NDB_Z, 6, TOL_F32), (capi.NDB, 6, TOL_F32), (capi.CN, 8, TOL_F32),
-                                              (capi.CN_F16, 8, TOL_BF16)])
-def test_symmetric_coupling_opt_in(variant, iters, tol):
+@pytest.mark.parametrize("B,variant,iters,tol", [(256, capi.NDB_Z, 6, TOL_F32), (256, capi.NDB, 6, TOL_F32),
+                                                (256, capi.CN, 8, TOL_F32), (256, capi.CN_F16, 8, TOL_BF16),
+                                                (768, capi.NDB_Z, 6, TOL_F32), (768, capi.CN, 6, TOL_F32)])
+def test_symmetric_coupling_opt_in(B, variant, iters, tol):
     """SHAMPOO_SYM_COUPLING forms Z Y (and C^p M) from upper tiles: on moderately
     conditioned factors and a few iterations it matches the oracle like the
     default, its residuals agree with the default's, and the roots are exactly
-    symmetric."""
-    nf, B = 4, 256
+    symmetric.  B = 768 runs Z Y on 3 x 3 tiles of the large kernel (three
+    diagonal tiles, reductions standing for mirrored tiles)."""
+    nf = 4
     F = W.spd_factors(160, nf, B, cond=1e3)
     V0 = W.start_vectors(161, nf, B)
     Fd = dev(F)
@@ -443,4 +445,4 @@ def test_symmetric_coupling_opt_in(variant, iters, tol):
     assert err <= tol, err
     # the weighted tile reductions give the same residual norms as the full products
     assert np.allclose(Rh, R0h, rtol=2e-2 if variant == capi.CN_F16 else 1e-3, atol=1e-4), (Rh, R0h)
-    report("sym_coupling", variant=variant, iters=iters, err=err)
+    report("sym_coupling", B=B, variant=variant, iters=iters, err=err)
