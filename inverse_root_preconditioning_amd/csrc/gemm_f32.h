@@ -1037,9 +1037,9 @@ struct EpiNdbE {
 struct EpiCnM {
   static constexpr bool kSym = true;
   static constexpr bool kDirect = false;
-  // full products on the large fp32 kernel with the epilogue through LDS (in
-  // registers it spills there); symmetric ones on the 128-wide kernel
-  static constexpr bool kBigSym = false, kBigFull = true;
+  // on the large fp32 kernel with the epilogue through LDS, full and
+  // symmetric products alike (in registers it spills there)
+  static constexpr bool kBigSym = true, kBigFull = true;
   static constexpr bool kBigStaged = true;
   // 16-bit: the 8-wave layout with its epilogue through LDS
   static constexpr bool kH16BigSym = true, kH16BigFull = true;
