@@ -886,7 +886,8 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
   int i2 = 0, i1 = 1, i0 = 2;  // ring slots of b_{j+2}, b_{j+1}, b_j
   int s1 = 0;                  // bf16 slot holding b_{j+1}
   if (bf) {
-    // b_d, b_{d-1} and the 16-bit operands in one pass (A_s is only needed as bf16)
+    // b_{d-1} and the 16-bit operands in one pass: A_s is needed only as bf16,
+    // and b_d = c_d I is formed by the first Clenshaw step
     Cheby16StartArgs s;
     s.x = F;
     s.sc = sc;
