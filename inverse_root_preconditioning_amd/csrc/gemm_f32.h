@@ -284,13 +284,16 @@ __device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, float
 // set are written.
 // KPRE bounds how many groups' epilogue inputs are loaded ahead (registers).
 //
-// SP > 0: the mirrored half goes through `stage`, this wave's 32 x (32 SP + 4)
-// floats of LDS.  Each group is first written there at its transposed place;
-// once the SP vertically adjacent blocks of one column are in, the wave reads
-// them back along the mirrored rows and each store instruction covers 32 SP
+// SP > 0: both halves go through `stage`, this wave's 32 x (32 SP + 4) floats
+// of LDS.  Each group is first written there at its transposed place; once
+// the SP vertically adjacent blocks of one column are in, the wave reads them
+// back along the mirrored rows, each store instruction covering 32 SP
 // consecutive columns of 64 / (8 SP) rows (whole 128-byte lines, where a
-// register-direct mirrored store covers 32 bytes of 32 rows).  On a diagonal
-// tile only entries of computed blocks strictly below the diagonal go out.
+// register-direct mirrored store covers 32 bytes of 32 rows), and along the
+// upper rows, 4 columns per lane (where group-wise upper stores take one
+// instruction per 1 or 2 bytes of 32 columns of 2 rows).  On a diagonal tile
+// only entries of computed blocks on (upper) or strictly below (mirrored) the
+// diagonal go out.
 // Groups are then taken column of blocks by column of blocks (j-major).
 template <int TM, int TN, int KPRE, int SP = 0, class Tile>
 __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[TM][TN], int m0, int n0, int wm,
@@ -317,17 +320,13 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
         if (r + e < c) tile.write(c, r + e, o[e]);
     }
   };
-  // Staged: the upper entries directly, the group into `stage`.  DG: a
-  // diagonal tile (compile-time, so that off-diagonal tiles carry no tests).
+  // Staged: the group goes into `stage` at its transposed place; both halves
+  // are written from there.  DG: a diagonal tile (compile-time, so that
+  // off-diagonal tiles carry no tests).
   auto emit_staged = [&](auto DG, auto G, const auto& o) __attribute__((always_inline)) {
     if constexpr (SP > 0) {
       constexpr int g = decltype(G)::value;
-      constexpr int i = gi_(g), j = gj_(g), q = g % 4;
-      const int r = m0 + wm + 32 * i + 8 * q + 4 * h;
-      const int c = n0 + wn + 32 * j + cl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (!decltype(DG)::value || r + e <= c) tile.write_upper(r + e, c, o[e]);
+      constexpr int i = gi_(g), q = g % 4;
       *reinterpret_cast<floatx4*>(stage + cl * LDT + 32 * (i % SP) + 8 * q + 4 * h) = o;
     }
   };
@@ -361,6 +360,27 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 if (r0 + cc + e < c0 + row) tile.write(c0 + row, r0 + cc + e, v[e]);
+            }
+          }
+        }
+        // The upper half along its own rows: 8 lanes per row, 4 columns each
+        // (a quarter of the store instructions of writing it group by group).
+        const int ru = lane >> 3, cu = 4 * (lane & 7);
+#pragma unroll 2
+        for (int t = 0; t < 4 * SP; ++t) {
+          const int rl = 8 * t + ru;
+          const floatx4 v = {stage[cu * LDT + rl], stage[(cu + 1) * LDT + rl], stage[(cu + 2) * LDT + rl],
+                             stage[(cu + 3) * LDT + rl]};
+          const int r = r0 + rl, c = c0 + cu;
+          if constexpr (!decltype(DG)::value) {
+            tile.write_upper4(r, c, v);
+          } else if ((mask >> ((i0 + rl / 32) * TN + j)) & 1) {
+            if (r <= c) {
+              tile.write_upper4(r, c, v);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (r <= c + e) tile.write_upper(r, c + e, v[e]);
             }
           }
         }
@@ -877,8 +897,9 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
 // inputs of the epilogue (an EMA state, Clenshaw terms) are symmetric too.
 // Those with kDirect also provide value4(r, c, v) for rows r..r+3 of column c,
 // write4t(c, r, o), which writes o to row c, columns r..r+3 (the mirrored
-// entries) with vector stores, and write_upper(row, col, o) for the computed
-// entries themselves.
+// entries) with vector stores, and write_upper(row, col, o) and
+// write_upper4(row, col, o) (columns col..col+3) for the computed entries
+// themselves.
 // ---------------------------------------------------------------------------
 
 // out = mult * acc + beta * cin (cin may alias out); X = I for a degenerate
@@ -947,6 +968,8 @@ struct EpiStore {
       if (o16) stg4_h16(o16 + idx, o, fmt);
     }
     __device__ __forceinline__ void write_upper(int row, int col, float o) { write(row, col, o); }
+    // row `row`, columns col..col+3, on or above the diagonal
+    __device__ __forceinline__ void write_upper4(int row, int col, const floatx4& o) { write4t(row, col, o); }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));
       return 0.f;
@@ -1207,6 +1230,15 @@ struct EpiClenshaw {
       const int64_t idx = (int64_t)row * B + col;
       if (obf == nullptr || is_final || row == col) stg(out + idx, o);
       if (obf) stg(obf + idx, to_h16(o, fmt));
+    }
+    // row `row`, columns col..col+3, on or above the diagonal
+    __device__ __forceinline__ void write_upper4(int row, int col, const floatx4& o) {
+      const int64_t idx = (int64_t)row * B + col;
+      if (obf == nullptr || is_final)
+        stg(reinterpret_cast<floatx4*>(out + idx), o);
+      else if (row >= col && row < col + 4)
+        stg(out + (int64_t)row * B + row, o[row - col]);
+      if (obf) stg4_h16(obf + idx, o, fmt);
     }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));
