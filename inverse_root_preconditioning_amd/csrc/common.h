@@ -109,6 +109,16 @@ __device__ __forceinline__ void stg4_h16(uint16_t* p, const floatx4& o, int fmt)
   stg(reinterpret_cast<u32x2*>(p), w);
 }
 
+// Eight consecutive 16-bit copies of lo, hi at p (p 16-byte aligned).
+__device__ __forceinline__ void stg8_h16(uint16_t* p, const floatx4& lo, const floatx4& hi, int fmt) {
+  u32x4 w;
+  w.x = (uint32_t)to_h16(lo[0], fmt) | ((uint32_t)to_h16(lo[1], fmt) << 16);
+  w.y = (uint32_t)to_h16(lo[2], fmt) | ((uint32_t)to_h16(lo[3], fmt) << 16);
+  w.z = (uint32_t)to_h16(hi[0], fmt) | ((uint32_t)to_h16(hi[1], fmt) << 16);
+  w.w = (uint32_t)to_h16(hi[2], fmt) | ((uint32_t)to_h16(hi[3], fmt) << 16);
+  stg(reinterpret_cast<u32x4*>(p), w);
+}
+
 __device__ __forceinline__ bool degenerate(int32_t st) {
   return (st & (SHAMPOO_BLK_ZERO | SHAMPOO_BLK_NONPOS_RQ)) != 0;
 }

@@ -290,7 +290,7 @@ __device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, float
 // back along the mirrored rows, each store instruction covering 32 SP
 // consecutive columns of 64 / (8 SP) rows (whole 128-byte lines, where a
 // register-direct mirrored store covers 32 bytes of 32 rows), and along the
-// upper rows, 4 columns per lane (where group-wise upper stores take one
+// upper rows, 4 or 8 columns per lane (where group-wise upper stores take one
 // instruction per 1 or 2 bytes of 32 columns of 2 rows).  On a diagonal tile
 // only entries of computed blocks on (upper) or strictly below (mirrored) the
 // diagonal go out.
@@ -363,26 +363,43 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
             }
           }
         }
-        // The upper half along its own rows: 8 lanes per row, 4 columns each
-        // (a quarter of the store instructions of writing it group by group).
-        const int ru = lane >> 3, cu = 4 * (lane & 7);
-#pragma unroll 2
-        for (int t = 0; t < 4 * SP; ++t) {
-          const int rl = 8 * t + ru;
-          const floatx4 v = {stage[cu * LDT + rl], stage[(cu + 1) * LDT + rl], stage[(cu + 2) * LDT + rl],
-                             stage[(cu + 3) * LDT + rl]};
-          const int r = r0 + rl, c = c0 + cu;
-          if constexpr (!decltype(DG)::value) {
-            tile.write_upper4(r, c, v);
-          } else if ((mask >> ((i0 + rl / 32) * TN + j)) & 1) {
-            if (r <= c) {
-              tile.write_upper4(r, c, v);
-            } else {
+        // The upper half along its own rows, CU columns per lane: 8 for block
+        // pairs (16-byte stores of the 16-bit copy), 4 for single blocks (a
+        // quarter or an eighth of the store instructions of writing it group
+        // by group; 8 measured slower for the fp32 kernel).
+        constexpr int CU = SP == 2 ? 8 : 4, LPU = 32 / CU, RPU = 64 / LPU;
+        const int ru = lane / LPU, cu = CU * (lane % LPU);
+        constexpr int NU = 32 * SP / RPU;  // iterations
+        auto upper = [&](int t) __attribute__((always_inline)) {
+          const int rl = RPU * t + ru;
+          floatx4 lo, hi;
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (r <= c + e) tile.write_upper(r, c + e, v[e]);
-            }
+          for (int e = 0; e < 4; ++e) lo[e] = stage[(cu + e) * LDT + rl];
+          if constexpr (CU == 8) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hi[e] = stage[(cu + 4 + e) * LDT + rl];
           }
+          const int r = r0 + rl, c = c0 + cu;
+          const bool whole = !decltype(DG)::value || r <= c;
+          const bool src = !decltype(DG)::value || ((mask >> ((i0 + rl / 32) * TN + j)) & 1);
+          if (src && whole) {
+            if constexpr (CU == 8)
+              tile.write_upper8(r, c, lo, hi);
+            else
+              tile.write_upper4(r, c, lo);
+          } else if (src) {
+#pragma unroll
+            for (int e = 0; e < CU; ++e)
+              if (r <= c + e) tile.write_upper(r, c + e, e < 4 ? lo[e & 3] : hi[e & 3]);
+          }
+        };
+        // one row group at a time for 8 columns, two for 4 (as measured fastest; more spills)
+        if constexpr (CU == 8) {
+#pragma unroll 1
+          for (int t = 0; t < NU; ++t) upper(t);
+        } else {
+#pragma unroll 2
+          for (int t = 0; t < NU; ++t) upper(t);
         }
         __builtin_amdgcn_wave_barrier();
       }
@@ -897,9 +914,9 @@ __global__ void __launch_bounds__(kBigThreads, 1) gemm_f32_big_kernel(const Gemm
 // inputs of the epilogue (an EMA state, Clenshaw terms) are symmetric too.
 // Those with kDirect also provide value4(r, c, v) for rows r..r+3 of column c,
 // write4t(c, r, o), which writes o to row c, columns r..r+3 (the mirrored
-// entries) with vector stores, and write_upper(row, col, o) and
-// write_upper4(row, col, o) (columns col..col+3) for the computed entries
-// themselves.
+// entries) with vector stores, and write_upper(row, col, o),
+// write_upper4(row, col, o) and write_upper8(row, col, lo, hi) (columns
+// col..col+3 or col..col+7) for the computed entries themselves.
 // ---------------------------------------------------------------------------
 
 // out = mult * acc + beta * cin (cin may alias out); X = I for a degenerate
@@ -968,8 +985,16 @@ struct EpiStore {
       if (o16) stg4_h16(o16 + idx, o, fmt);
     }
     __device__ __forceinline__ void write_upper(int row, int col, float o) { write(row, col, o); }
-    // row `row`, columns col..col+3, on or above the diagonal
+    // row `row`, columns col..col+3 (col..col+7), on or above the diagonal
     __device__ __forceinline__ void write_upper4(int row, int col, const floatx4& o) { write4t(row, col, o); }
+    __device__ __forceinline__ void write_upper8(int row, int col, const floatx4& lo, const floatx4& hi) {
+      const int64_t idx = (int64_t)row * B + col;
+      if (out) {
+        stg(reinterpret_cast<floatx4*>(out + idx), lo);
+        stg(reinterpret_cast<floatx4*>(out + idx + 4), hi);
+      }
+      if (o16) stg8_h16(o16 + idx, lo, hi, fmt);
+    }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));
       return 0.f;
@@ -1231,7 +1256,7 @@ struct EpiClenshaw {
       if (obf == nullptr || is_final || row == col) stg(out + idx, o);
       if (obf) stg(obf + idx, to_h16(o, fmt));
     }
-    // row `row`, columns col..col+3, on or above the diagonal
+    // row `row`, columns col..col+3 (col..col+7), on or above the diagonal
     __device__ __forceinline__ void write_upper4(int row, int col, const floatx4& o) {
       const int64_t idx = (int64_t)row * B + col;
       if (obf == nullptr || is_final)
@@ -1239,6 +1264,17 @@ struct EpiClenshaw {
       else if (row >= col && row < col + 4)
         stg(out + (int64_t)row * B + row, o[row - col]);
       if (obf) stg4_h16(obf + idx, o, fmt);
+    }
+    __device__ __forceinline__ void write_upper8(int row, int col, const floatx4& lo, const floatx4& hi) {
+      const int64_t idx = (int64_t)row * B + col;
+      if (obf == nullptr || is_final) {
+        stg(reinterpret_cast<floatx4*>(out + idx), lo);
+        stg(reinterpret_cast<floatx4*>(out + idx + 4), hi);
+      } else if (row >= col && row < col + 8) {
+        const int e = row - col;
+        stg(out + (int64_t)row * B + row, e < 4 ? lo[e & 3] : hi[e & 3]);
+      }
+      if (obf) stg8_h16(obf + idx, lo, hi, fmt);
     }
     __device__ __forceinline__ float store(int row, int col, float v) {
       write(row, col, value(row, col, v));
