@@ -344,6 +344,24 @@ def test_repeat_runs_are_bitwise_identical():
         assert np.array_equal(a, b)
 
 
+def test_repeat_runs_are_bitwise_identical_large_tiles():
+    """The same on 2 x 2 large tiles: power iteration by columns, Newton-DB on
+    the fp32 large kernel and bf16 Chebyshev on the 8-wave 16-bit kernel with
+    their LDS-staged symmetric epilogues (fixed reduction orders throughout)."""
+    nf, B = 3, 512
+    F = W.spd_factors(92, nf, B, cond=1e4)
+    V0 = W.start_vectors(93, nf, B)
+    Fd, Vd = dev(F), dev(V0)
+    outs = []
+    for _ in range(2):
+        sc, st = gpu_scale(Fd, 1e-12, capi.SCALE_POWER, Vd)
+        X, R = gpu_roots(Fd, sc, st, "newton", iters=5, variant=capi.NDB_Z, resid=True)
+        Xc, _ = gpu_roots(Fd, sc, st, "cheby", degree=12, prec=capi.BF16_IN)
+        outs.append((host(sc), host(X), host(R), host(Xc)))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("full", [False, True])
 @pytest.mark.parametrize("B", [128, 256])
 @pytest.mark.parametrize("p,iters", [(4, 1), (4, 2), (4, 6), (4, 12), (1, 6), (2, 6), (8, 6)])
