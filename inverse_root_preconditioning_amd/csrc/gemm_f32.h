@@ -481,7 +481,7 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
 // Workgroup lid -> (job, item, tile row tm, tile column tn), item-major: the
 // tiles of both jobs of one item are neighbours, so that the workgroups that
 // run together share that item's operands (E in Y E and E Z) through L2.  A
-// symmetric product enumerates only its upper tiles (tm <= tn), row by row.
+// symmetric product enumerates only its upper tiles (tm <= tn).
 template <bool SYM, class L>
 __device__ __forceinline__ void decode_tile(const L& P, uint32_t lid, int& job, int64_t& item, int& tm,
                                             int& tn) {
@@ -495,14 +495,21 @@ __device__ __forceinline__ void decode_tile(const L& P, uint32_t lid, int& job, 
     tm = t / P.tiles_n;
     tn = t - tm * P.tiles_n;
   } else {
-    tm = 0;
-    int rowlen = P.tiles_n;
-    while (t >= rowlen) {
-      t -= rowlen;
-      ++tm;
-      --rowlen;
+    // the off-diagonal tiles row by row, then the diagonal ones, which are
+    // shorter: the last workgroups of a launch are then the shortest
+    const int noff = P.tiles_n * (P.tiles_n - 1) / 2;
+    if (t >= noff) {
+      tm = tn = t - noff;
+    } else {
+      tm = 0;
+      int rowlen = P.tiles_n - 1;
+      while (t >= rowlen) {
+        t -= rowlen;
+        ++tm;
+        --rowlen;
+      }
+      tn = tm + 1 + t;
     }
-    tn = tm + t;
   }
 }
 
