@@ -489,18 +489,20 @@ __device__ __forceinline__ void decode_tile(const L& P, uint32_t lid, int& job, 
   const uint32_t njobs = P.total / ((uint32_t)P.nitems * tpi);
   item = lid / (njobs * tpi);
   const uint32_t rem = lid - (uint32_t)item * njobs * tpi;
-  job = rem / tpi;
-  int t = rem - job * tpi;
   if constexpr (!SYM) {
+    job = rem / tpi;
+    const int t = rem - job * tpi;
     tm = t / P.tiles_n;
     tn = t - tm * P.tiles_n;
   } else {
-    // the off-diagonal tiles row by row, then the diagonal ones, which are
-    // shorter: the last workgroups of a launch are then the shortest
-    const int noff = P.tiles_n * (P.tiles_n - 1) / 2;
-    if (t >= noff) {
-      tm = tn = t - noff;
-    } else {
+    // the off-diagonal tiles of every job row by row, then the diagonal ones,
+    // which are shorter (about 0.65 of a tile; measured 4% faster for the
+    // Newton-DB pair than row order; the diagonal tiles of all factors at the
+    // end of the launch lose the operands' L2 reuse and measured 23% slower)
+    const uint32_t noff = (uint32_t)(P.tiles_n * (P.tiles_n - 1) / 2);
+    if (rem < njobs * noff) {
+      job = rem / noff;
+      int t = rem - job * noff;
       tm = 0;
       int rowlen = P.tiles_n - 1;
       while (t >= rowlen) {
@@ -509,6 +511,10 @@ __device__ __forceinline__ void decode_tile(const L& P, uint32_t lid, int& job, 
         --rowlen;
       }
       tn = tm + 1 + t;
+    } else {
+      const uint32_t r2 = rem - njobs * noff;
+      job = r2 / P.tiles_n;
+      tm = tn = r2 - job * P.tiles_n;
     }
   }
 }
