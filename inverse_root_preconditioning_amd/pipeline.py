@@ -25,6 +25,8 @@ def _ptr(t):
 
 
 def _check_f32_cuda(t, name, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
     if not (t.is_cuda and t.dtype == torch.float32 and t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous float32 CUDA tensor")
     if shape is not None and tuple(t.shape) != tuple(shape):

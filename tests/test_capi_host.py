@@ -144,3 +144,12 @@ def test_graft_validation_without_gpu():
 def test_binding_raises_when_library_missing(tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         capi.load(str(tmp_path / "missing.so"))
+
+
+def test_pipeline_rejects_missing_or_host_tensors():
+    import torch
+    from inverse_root_preconditioning_amd import pipeline
+    with pytest.raises(ValueError, match="v0 is required"):
+        pipeline._check_f32_cuda(None, "v0")
+    with pytest.raises(ValueError, match="CUDA tensor"):
+        pipeline._check_f32_cuda(torch.zeros(2, 4, 4), "factors")
