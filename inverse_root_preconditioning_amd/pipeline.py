@@ -33,6 +33,25 @@ def _check_f32_cuda(t, name, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _check_scale_status(scale, status, nf):
+    """scale: [nf, 4] float32 (c, eps, lambda, trace); status: [nf] int32."""
+    _check_f32_cuda(scale, "scale", (nf, 4))
+    if status is None:
+        raise ValueError("status is required")
+    if not (status.is_cuda and status.dtype == torch.int32 and status.is_contiguous()):
+        raise ValueError("status must be a contiguous int32 CUDA tensor")
+    if tuple(status.shape) != (nf,):
+        raise ValueError(f"status has shape {tuple(status.shape)}, expected {(nf,)}")
+
+
+def residual_columns(p, variant, iters):
+    """Columns of resid_out for shampoo_invroot_newton: one per iteration of
+    each pass (Newton-DB for p = 4 runs two passes, p = 2 and coupled Newton one)."""
+    base = variant & 0xff
+    passes = 1 if (p == 2 or base in (capi.CN, capi.CN_F16)) else 2
+    return passes * iters
+
+
 class BlockTable:
     """Device array of shampoo_block descriptors (24 bytes each) plus the
     tensors it points into (kept alive with the table)."""
@@ -113,8 +132,9 @@ def new_scale(nf, device):
 
 
 def scale_power(factors, eps_rel, mode, v0, steps, safety, scale, status, ws=None, stream=None):
-    nf, B, _ = factors.shape
     _check_f32_cuda(factors, "factors")
+    nf, B, _ = factors.shape
+    _check_scale_status(scale, status, nf)
     r = 0
     if mode == capi.SCALE_POWER:
         _check_f32_cuda(v0, "v0")
@@ -129,9 +149,12 @@ def scale_power(factors, eps_rel, mode, v0, steps, safety, scale, status, ws=Non
 
 
 def invroot_newton(factors, scale, p, variant, iters, x_out, status, resid_out=None, ws=None, stream=None):
-    nf, B, _ = factors.shape
     _check_f32_cuda(factors, "factors")
+    nf, B, _ = factors.shape
     _check_f32_cuda(x_out, "x_out", factors.shape)
+    _check_scale_status(scale, status, nf)
+    if resid_out is not None:
+        _check_f32_cuda(resid_out, "resid_out", (nf, residual_columns(p, variant, iters)))
     ws = ws or Workspace(factors.device)
     wp, wb = ws.get(capi.shampoo_workspace_bytes(capi.OP_NEWTON, nf, B, variant, F32))
     capi.check(capi.shampoo_invroot_newton(factors.data_ptr(), scale.data_ptr(), nf, B, p, variant, iters,
@@ -140,9 +163,10 @@ def invroot_newton(factors, scale, p, variant, iters, x_out, status, resid_out=N
 
 
 def invroot_cheby(factors, scale, p, degree, interval_eps, prec, x_out, status, ws=None, stream=None):
-    nf, B, _ = factors.shape
     _check_f32_cuda(factors, "factors")
+    nf, B, _ = factors.shape
     _check_f32_cuda(x_out, "x_out", factors.shape)
+    _check_scale_status(scale, status, nf)
     ws = ws or Workspace(factors.device)
     wp, wb = ws.get(capi.shampoo_workspace_bytes(capi.OP_CHEBY, nf, B, degree, prec))
     capi.check(capi.shampoo_invroot_cheby(factors.data_ptr(), scale.data_ptr(), nf, B, p, degree, interval_eps,
@@ -219,8 +243,8 @@ class ShampooBlocks:
         self.scale, self.status = new_scale(2 * n, dev)
         self.resid = None
         if self.cfg.keep_resid and self.cfg.solver == "newton":
-            passes = 1 if (self.cfg.p == 2 or (self.cfg.variant & 0xff) in (capi.CN, capi.CN_F16)) else 2
-            self.resid = torch.zeros((2 * n, passes * self.cfg.iters), dtype=torch.float32, device=dev)
+            cols = residual_columns(self.cfg.p, self.cfg.variant, self.cfg.iters)
+            self.resid = torch.zeros((2 * n, cols), dtype=torch.float32, device=dev)
         self.ws = {k: Workspace(dev) for k in ("acc", "scale", "root", "pre")}
         self.v0 = None
         if self.cfg.update_every < 1:

@@ -246,18 +246,29 @@ def invroot_coupled_newton(A_s, p, iters):
     reading follows [GH]: X_0 = I, M_0 = A_s, C_k = ((p+1) I - M_k) / p.
     The iteration converges for spectra inside (0, p+1).
     """
+    return coupled_newton(A_s, p, iters)[0]
+
+
+def coupled_newton(A_s, p, iters):
+    """The coupled Newton iteration of invroot_coupled_newton with its
+    residuals: returns (X, residuals), residuals[i] = ||I - M_i||_F at
+    iteration i (before its update).  M_k tends to I as X_k tends to
+    A_s^{-1/p} (M_k = X_k^p A_s in exact arithmetic), so the distance of M
+    from I measures convergence the way ||I - Z Y||_F does for Newton-DB."""
     M = _f64(A_s).copy()
     n = M.shape[0]
     I = np.eye(n)
     X = I.copy()
+    res = []
     for _ in range(iters):
+        res.append(math.sqrt(float(np.sum((I - M) ** 2))))
         C = ((p + 1) * I - M) / p
         X = X @ C
         Cp = I.copy()
         for _ in range(p):
             Cp = Cp @ C
         M = Cp @ M
-    return X
+    return X, res
 
 
 def chebyshev_coefficients(degree, p, delta):
@@ -516,13 +527,20 @@ def ndb_scalar(a, iters, chaining="Y"):
 
 
 def cn_scalar(a, p, iters):
+    return cn_scalar_trace(a, p, iters)[0]
+
+
+def cn_scalar_trace(a, p, iters):
+    """Scalar coupled Newton: (x after `iters` iterations, [m_0, ..., m_{iters-1}])."""
     m = np.array(a, dtype=F64)
     x = np.ones_like(m)
+    ms = []
     for _ in range(iters):
+        ms.append(m.copy())
         q = ((p + 1) - m) / p
         x = x * q
         m = q ** p * m
-    return x
+    return x, ms
 
 
 def cheby_scalar(a, coeffs):

@@ -153,3 +153,12 @@ def test_pipeline_rejects_missing_or_host_tensors():
         pipeline._check_f32_cuda(None, "v0")
     with pytest.raises(ValueError, match="CUDA tensor"):
         pipeline._check_f32_cuda(torch.zeros(2, 4, 4), "factors")
+
+
+def test_residual_columns_follow_the_passes():
+    from inverse_root_preconditioning_amd import pipeline
+    assert pipeline.residual_columns(4, capi.NDB, 10) == 20
+    assert pipeline.residual_columns(4, capi.NDB_Z | capi.SYM_COUPLING, 7) == 14
+    assert pipeline.residual_columns(2, capi.NDB, 10) == 10
+    assert pipeline.residual_columns(4, capi.CN | capi.FULL_PRODUCTS, 12) == 12
+    assert pipeline.residual_columns(8, capi.CN_F16, 5) == 5

@@ -91,6 +91,42 @@ def test_exact_root_invariants(cond):
 
 
 # ---------------------------------------------------------------------------
+# The parity measure and the residual (every GPU parity bound rests on these)
+# ---------------------------------------------------------------------------
+
+def test_relative_frobenius_closed_form():
+    g = golden()["relative_frobenius_pin"]
+    x, ref = np.array(g["x"]), np.array(g["ref"])
+    assert abs(O.relative_frobenius(x, ref) - g["value"]) <= 1e-16
+    # the denominator is the reference's norm, not the candidate's
+    assert O.relative_frobenius(np.eye(4), 2 * np.eye(4)) == 0.5
+    assert O.relative_frobenius(2 * np.eye(4), np.eye(4)) == 1.0
+    # scale invariance and zero distance
+    assert abs(O.relative_frobenius(1e-20 * x, 1e-20 * ref) - g["value"]) <= 1e-16
+    assert O.relative_frobenius(ref, ref) == 0.0
+    # a 3 x 3 case with every entry off by 0.1: ||x - ref||_F = sqrt(9 * 0.01) = 0.3, ||ref||_F = 3
+    ref3 = np.eye(3) * math.sqrt(3.0)
+    assert abs(O.relative_frobenius(ref3 + 0.1, ref3) - 0.1) <= 1e-15
+
+
+def test_residual_fourth_closed_forms():
+    g = golden()["residual_fourth_pin"]
+    assert abs(O.residual_fourth(np.array(g["X"]), np.array(g["A"])) - g["value"]) <= 1e-15
+    for n in (1, 4, 9):
+        # X^4 A - I = 2I - I = I
+        assert abs(O.residual_fourth(np.eye(n), 2 * np.eye(n)) - math.sqrt(n)) <= 1e-15
+        # the exact root of 2I leaves no residual
+        assert O.residual_fourth(2 ** -0.25 * np.eye(n), 2 * np.eye(n)) <= 4e-16 * math.sqrt(n)
+    # a non-diagonal case: A = Q diag(1, 16) Q^T and X = Q diag(1, 1/4) Q^T has X^4 A = Q diag(1, 1/16) Q^T,
+    # residual ||diag(0, -15/16)||_F = 15/16 whatever the rotation Q
+    c, s = math.cos(0.3), math.sin(0.3)
+    Q = np.array([[c, -s], [s, c]])
+    A = Q @ np.diag([1.0, 16.0]) @ Q.T
+    X = Q @ np.diag([1.0, 0.25]) @ Q.T
+    assert abs(O.residual_fourth(X, A) - 15.0 / 16.0) <= 1e-14
+
+
+# ---------------------------------------------------------------------------
 # Newton-DB
 # ---------------------------------------------------------------------------
 
@@ -155,6 +191,29 @@ def test_cn_golden_first_iteration():
     assert X[0, 0] == g["x1"]
     q = g["x1"]
     assert q ** g["p"] * g["a"] == g["m1"]
+
+
+def test_cn_residuals_golden_and_first_entry():
+    g = golden()["cn_residuals_a_half_p4"]
+    X, res = O.coupled_newton(np.array([[g["a"]]]), g["p"], 2)
+    assert res == g["residuals"]
+    A, _, _ = rand_spd(6, 8, 10.0)
+    A_s = A / (2 * np.linalg.eigvalsh(A).max())
+    _, res = O.coupled_newton(A_s, 4, 3)
+    assert abs(res[0] - np.linalg.norm(np.eye(8) - A_s)) <= 1e-14
+    assert np.array_equal(O.coupled_newton(A_s, 4, 5)[0], O.invroot_coupled_newton(A_s, 4, 5))
+
+
+def test_cn_residuals_equal_spectral_map():
+    """||I - M_k||_F = sqrt(sum_j (1 - m_k(lambda_j))^2) over the eigenvalues
+    (M_k is a polynomial in A_s), and it falls to 0 as the iteration converges."""
+    A, _, lam = rand_spd(9, 16, 1e3)
+    top = 2 * lam.max()
+    _, res = O.coupled_newton(A / top, 4, 12)
+    _, ms = O.cn_scalar_trace(lam / top, 4, 12)
+    ref = [math.sqrt(float(np.sum((1.0 - m) ** 2))) for m in ms]
+    assert np.allclose(res, ref, rtol=1e-11, atol=1e-13)
+    assert res[-1] < 1e-3 * res[0]
 
 
 @pytest.mark.parametrize("p", [2, 4])
