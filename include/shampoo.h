@@ -28,7 +28,8 @@
  *    memory comes from the caller's workspace `ws` of `ws_bytes` bytes (size from
  *    shampoo_workspace_bytes); it must stay allocated until the stream has
  *    executed the call, and one workspace must not be shared by calls that may
- *    run concurrently.
+ *    run concurrently.  (shampoo_graft_update_noalloc takes no workspace: it
+ *    uses a static device array of the library instead.)
  *  - Argument errors are returned synchronously as negative codes and nothing is
  *    enqueued.  A count of 0 (no blocks / factors) is a valid no-op.
  *  - Numerical trouble is reported per factor in a caller int32 status array on
@@ -56,7 +57,8 @@ enum {
   SHAMPOO_EINVAL = -1,        /* a null pointer, a negative count, a parameter out of range */
   SHAMPOO_EUNSUPPORTED = -2,  /* a valid value this library does not implement (B, p, prec) */
   SHAMPOO_EWORKSPACE = -3,    /* workspace missing or smaller than shampoo_workspace_bytes */
-  SHAMPOO_EHIP = -4           /* the HIP runtime refused a launch */
+  SHAMPOO_EHIP = -4,          /* the HIP runtime refused a launch */
+  SHAMPOO_ESCRATCH = -5       /* larger than the static scratch of shampoo_graft_update_noalloc */
 };
 
 /* Per-factor status bits (int32 status[nfactors] on the device). */
@@ -275,6 +277,30 @@ int shampoo_graft_update(const shampoo_block* g_blocks, const shampoo_block* u_b
                          const shampoo_block* v_blocks, int64_t nblocks, int B, float lr, float beta1,
                          float beta2, float eps, int step, float* scale_out,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * shampoo_graft_update_noalloc -- shampoo_graft_update without a workspace.
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The
+ * per-block partial norms live in a static device array of
+ * SHAMPOO_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends; this call allocates nothing and frees nothing.
+ * Arguments, results and errors are those of shampoo_graft_update, plus
+ * SHAMPOO_ESCRATCH (nothing enqueued) when the partial norms need more than
+ * the static array: nblocks * min(max(B / 64, 1), 64) * 8 bytes, rounded up to
+ * 256, must not exceed SHAMPOO_NOALLOC_SCRATCH_BYTES (e.g. up to 8192 blocks
+ * at B = 1024).  The array starts with no meaningful contents and every call
+ * overwrites all of the part it reads before reading it.  All calls on one
+ * GPU share that GPU's array: calls that may overlap in time on the same GPU
+ * (different streams, or different host threads without ordering) race and
+ * must not be issued.  The first call on a device looks up the array's
+ * address there (SHAMPOO_EHIP if that fails).
+ */
+#define SHAMPOO_NOALLOC_SCRATCH_BYTES (1u << 20)
+int shampoo_graft_update_noalloc(const shampoo_block* g_blocks, const shampoo_block* u_blocks,
+                                 const shampoo_block* param_blocks, const shampoo_block* m_blocks,
+                                 const shampoo_block* v_blocks, int64_t nblocks, int B, float lr, float beta1,
+                                 float beta2, float eps, int step, float* scale_out, hipStream_t stream);
 
 /* Workspace size in bytes for an operation (op = SHAMPOO_OP_*).  `count` is
  * nfactors for SCALE/NEWTON/CHEBY and nblocks for ACCUMULATE/PRECONDITION;

@@ -21,6 +21,8 @@ EINVAL = -1
 EUNSUPPORTED = -2
 EWORKSPACE = -3
 EHIP = -4
+ESCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 1 << 20
 # Per-factor status bits
 BLK_NONFINITE = 1
 BLK_ZERO = 2
@@ -90,6 +92,8 @@ _SIGNATURES = {
     "shampoo_graft_update": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int,
                                      c_float, c_float, c_float, c_float, c_int, c_void_p,
                                      c_void_p, c_size_t, c_void_p]),
+    "shampoo_graft_update_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int,
+                                             c_float, c_float, c_float, c_float, c_int, c_void_p, c_void_p]),
 }
 
 EXPORTED = tuple(_SIGNATURES)
@@ -178,3 +182,9 @@ def shampoo_graft_update(g_blocks, u_blocks, param_blocks, m_blocks, v_blocks, n
                          eps, step, scale_out, ws, ws_bytes, stream):
     return load().shampoo_graft_update(g_blocks, u_blocks, param_blocks, m_blocks, v_blocks, nblocks, B, lr,
                                        beta1, beta2, eps, step, scale_out, ws, ws_bytes, stream)
+
+
+def shampoo_graft_update_noalloc(g_blocks, u_blocks, param_blocks, m_blocks, v_blocks, nblocks, B, lr, beta1,
+                                 beta2, eps, step, scale_out, stream):
+    return load().shampoo_graft_update_noalloc(g_blocks, u_blocks, param_blocks, m_blocks, v_blocks, nblocks, B,
+                                               lr, beta1, beta2, eps, step, scale_out, stream)

@@ -5,6 +5,7 @@
 // nothing is allocated and nothing synchronises.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "gemm_bf16.h"
 #include "kernels_misc.h"
@@ -15,6 +16,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kMaxB = 16384;
+constexpr size_t kScratchBytes = SHAMPOO_NOALLOC_SCRATCH_BYTES;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -972,6 +974,9 @@ const char* shampoo_strerror(int code) {
     case SHAMPOO_EUNSUPPORTED: return "unsupported configuration (B must be a multiple of 64 in [64, 16384])";
     case SHAMPOO_EWORKSPACE: return "workspace missing or smaller than shampoo_workspace_bytes";
     case SHAMPOO_EHIP: return "HIP runtime error while launching a kernel";
+    case SHAMPOO_ESCRATCH:
+      return "problem too large for the static scratch of the allocation-free entry point "
+             "(SHAMPOO_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown shampoo error code";
   }
 }
@@ -1203,11 +1208,13 @@ int shampoo_precondition(const float* x_roots, const shampoo_block* g_blocks, in
 
 }  // extern "C"
 
-extern "C" int shampoo_graft_update(const shampoo_block* g_blocks, const shampoo_block* u_blocks,
-                                    const shampoo_block* param_blocks, const shampoo_block* m_blocks,
-                                    const shampoo_block* v_blocks, int64_t nblocks, int B, float lr, float beta1,
-                                    float beta2, float eps, int step, float* scale_out, void* ws,
-                                    size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+// Validation and launch shared by the two grafting entry points; `partials`
+// is null only while validating.
+int graft_check(const shampoo_block* g_blocks, const shampoo_block* u_blocks, const shampoo_block* param_blocks,
+                const shampoo_block* m_blocks, const shampoo_block* v_blocks, int64_t nblocks, int B, float lr,
+                float beta1, float beta2, float eps, int step) {
   if (nblocks < 0) return SHAMPOO_EINVAL;
   if (!valid_B(B)) return SHAMPOO_EUNSUPPORTED;
   if (!std::isfinite(lr) || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) || !(eps >= 0.f) ||
@@ -1215,15 +1222,18 @@ extern "C" int shampoo_graft_update(const shampoo_block* g_blocks, const shampoo
     return SHAMPOO_EINVAL;
   if (nblocks == 0) return SHAMPOO_OK;
   if (!g_blocks || !u_blocks || !param_blocks || !m_blocks || !v_blocks) return SHAMPOO_EINVAL;
-  Carver cm(nullptr);
-  const size_t need = graft_layout(cm, nblocks, B, nullptr);
-  if (ws == nullptr || ws_bytes < need) return SHAMPOO_EWORKSPACE;
+  if ((uint64_t)nblocks * graft_chunks(B) > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
+  return SHAMPOO_OK;
+}
+
+int graft_launch(const shampoo_block* g_blocks, const shampoo_block* u_blocks, const shampoo_block* param_blocks,
+                 const shampoo_block* m_blocks, const shampoo_block* v_blocks, int64_t nblocks, int B, float lr,
+                 float beta1, float beta2, float eps, int step, float* scale_out, float* partials,
+                 hipStream_t stream) {
   const int chunks = graft_chunks(B);
-  if ((uint64_t)nblocks * chunks > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
-  Carver c(ws);
   GraftArgs a;
   memset(&a, 0, sizeof(a));
-  graft_layout(c, nblocks, B, &a.partials);
+  a.partials = partials;
   a.g = g_blocks;
   a.u = u_blocks;
   a.theta = param_blocks;
@@ -1243,4 +1253,71 @@ extern "C" int shampoo_graft_update(const shampoo_block* g_blocks, const shampoo
   SHP_TRY(check_launch());
   hipLaunchKernelGGL(graft_apply_kernel, grid, dim3(256), 0, stream, a);
   return check_launch();
+}
+
+constexpr size_t kScratchFloats = kScratchBytes / sizeof(float);
+
+}  // namespace
+
+// Scratch of shampoo_graft_update_noalloc: the per-chunk partial sums of the
+// grafting norms, 2 floats per (block, chunk).  Every GPU the library runs on
+// holds its own copy until the process ends.  Host code never uses this name
+// as an address: it takes the device address from g_scratch_ptr.
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch`, looked up once per device.
+int scratch_address(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SHAMPOO_EHIP;
+  if (dev >= kMaxDevices) return SHAMPOO_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SHAMPOO_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<float*>(g_scratch_ptr[dev]);
+  return SHAMPOO_OK;
+}
+
+}  // namespace
+
+extern "C" int shampoo_graft_update(const shampoo_block* g_blocks, const shampoo_block* u_blocks,
+                                    const shampoo_block* param_blocks, const shampoo_block* m_blocks,
+                                    const shampoo_block* v_blocks, int64_t nblocks, int B, float lr, float beta1,
+                                    float beta2, float eps, int step, float* scale_out, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  SHP_TRY(graft_check(g_blocks, u_blocks, param_blocks, m_blocks, v_blocks, nblocks, B, lr, beta1, beta2, eps,
+                      step));
+  if (nblocks == 0) return SHAMPOO_OK;
+  Carver cm(nullptr);
+  const size_t need = graft_layout(cm, nblocks, B, nullptr);
+  if (ws == nullptr || ws_bytes < need) return SHAMPOO_EWORKSPACE;
+  Carver c(ws);
+  float* partials = nullptr;
+  graft_layout(c, nblocks, B, &partials);
+  return graft_launch(g_blocks, u_blocks, param_blocks, m_blocks, v_blocks, nblocks, B, lr, beta1, beta2, eps, step,
+                      scale_out, partials, stream);
+}
+
+extern "C" int shampoo_graft_update_noalloc(const shampoo_block* g_blocks, const shampoo_block* u_blocks,
+                                            const shampoo_block* param_blocks, const shampoo_block* m_blocks,
+                                            const shampoo_block* v_blocks, int64_t nblocks, int B, float lr,
+                                            float beta1, float beta2, float eps, int step, float* scale_out,
+                                            hipStream_t stream) {
+  SHP_TRY(graft_check(g_blocks, u_blocks, param_blocks, m_blocks, v_blocks, nblocks, B, lr, beta1, beta2, eps,
+                      step));
+  if (nblocks == 0) return SHAMPOO_OK;
+  Carver cm(nullptr);
+  if (graft_layout(cm, nblocks, B, nullptr) > kScratchBytes) return SHAMPOO_ESCRATCH;
+  float* partials = nullptr;
+  SHP_TRY(scratch_address(&partials));
+  return graft_launch(g_blocks, u_blocks, param_blocks, m_blocks, v_blocks, nblocks, B, lr, beta1, beta2, eps, step,
+                      scale_out, partials, stream);
 }

@@ -162,3 +162,16 @@ def test_residual_columns_follow_the_passes():
     assert pipeline.residual_columns(2, capi.NDB, 10) == 10
     assert pipeline.residual_columns(4, capi.CN | capi.FULL_PRODUCTS, 12) == 12
     assert pipeline.residual_columns(8, capi.CN_F16, 5) == 5
+
+
+def test_noalloc_graft_rejects_oversized_problems_without_gpu():
+    """The allocation-free grafting call refuses, before any HIP call, a problem
+    whose partial norms exceed its static scratch (1 MiB: 8192 blocks at
+    B = 1024, whose 16 row chunks take 128 bytes per block)."""
+    f = capi
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    limit = f.NOALLOC_SCRATCH_BYTES // 128
+    assert f.shampoo_graft_update_noalloc(*args, limit + 1, 1024, 1e-3, 0.9, 0.95, 1e-8, 1, 0, 0) == f.ESCRATCH
+    assert "static scratch" in f.shampoo_strerror(f.ESCRATCH)
+    assert f.shampoo_graft_update_noalloc(*args, 3, 1024, 1e-3, 0.9, 0.95, 1e-8, 0, 0, 0) == f.EINVAL  # step 0
+    assert f.shampoo_graft_update_noalloc(0, 0, 0, 0, 0, 0, 1024, 1e-3, 0.9, 0.95, 1e-8, 1, 0, 0) == f.OK
