@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define SHAMPOO_ABI_VERSION 1
+#define SHAMPOO_ABI_VERSION 2
 
 /* Return codes. */
 enum {
@@ -65,7 +65,12 @@ enum {
 enum {
   SHAMPOO_BLK_NONFINITE = 1,  /* trace, spectral estimate or an iterate is not finite; values propagate */
   SHAMPOO_BLK_ZERO = 2,       /* tr(F) == 0 (all-zero history): X = I is returned */
-  SHAMPOO_BLK_NONPOS_RQ = 4   /* spectral estimate <= 0: X = I is returned */
+  SHAMPOO_BLK_NONPOS_RQ = 4,  /* spectral estimate <= 0: X = I is returned */
+  SHAMPOO_BLK_RESID_GROWTH = 8 /* a Newton residual rose above twice the smallest earlier residual of its
+                                  pass: rounding errors are growing (the iteration diverges in this
+                                  precision); X is still returned.  [DASH] "Limitations" and
+                                  "Scoreboard with context" name unstable low-precision and
+                                  Frobenius-scaled Newton runs; the pages give no detector */
 };
 
 /* Operand precision of the matrix products. */
@@ -211,7 +216,13 @@ int shampoo_scale_power(const float* factors, int64_t nfactors, int B, float eps
  *              each Newton-DB iteration (passes = 1 for p = 2, else 2), or
  *              ||I - M||_F before each coupled-Newton iteration (passes = 1)
  *   status     device int32[nfactors]; factors flagged ZERO or NONPOS_RQ get
- *              X = I; NONFINITE is added when a residual is not finite
+ *              X = I; NONFINITE is added when a residual is not finite, and
+ *              RESID_GROWTH when a residual exceeds twice the smallest earlier
+ *              residual of the same pass (in exact arithmetic the residuals of a
+ *              pass never increase for a spectrum inside the iteration's
+ *              convergence region, (0, 3) for Newton-DB and (0, p + 1) for
+ *              coupled Newton).  The residuals are computed whether or not
+ *              resid_out is given.
  *   ws         shampoo_workspace_bytes(SHAMPOO_OP_NEWTON, nfactors, B, variant, SHAMPOO_F32)
  */
 int shampoo_invroot_newton(const float* factors, const shampoo_scale* scale,
@@ -315,26 +326,29 @@ const char* shampoo_strerror(int code);
 /* SHAMPOO_ABI_VERSION of the built library. */
 int shampoo_abi_version(void);
 
-/* Kernel families for shampoo_timing_hook. */
+/* Kernel families for shampoo_timing_hook (bits, OR-able). */
 enum {
   SHAMPOO_TIME_OFF = 0,
   SHAMPOO_TIME_NDB_PAIR = 1,   /* Newton-DB updates Y E and E Z, launched together (2 products) */
   SHAMPOO_TIME_NDB_P = 2,      /* Newton-DB product Z Y with the E = (3I - P)/2 epilogue */
-  SHAMPOO_TIME_CLENSHAW = 3,   /* one Clenshaw product A_s b (fp32 or bf16) */
-  SHAMPOO_TIME_CN_M = 4        /* coupled Newton's product C^p M (fp32 or fp16) */
+  SHAMPOO_TIME_CLENSHAW = 4,   /* one Clenshaw product A_s b (fp32 or bf16) */
+  SHAMPOO_TIME_CN_M = 8,       /* coupled Newton's product C^p M (fp32 or fp16) */
+  SHAMPOO_TIME_ALL = 15
 };
 
 /*
  * shampoo_timing_hook -- measurement instrumentation (not part of the method).
- * While enabled, each launch of kernel family `family` made by any later call
- * records events[2 i] just before and events[2 i + 1] just after the launch on
- * that call's stream, for i < capacity; further launches are not recorded.
- * `events` are caller-created HIP events (2 * capacity of them) that must
- * outlive the recorded launches.  family = SHAMPOO_TIME_OFF disables the hook.
- * The hook is process-wide and not thread-safe; enabling it resets the count.
+ * While enabled, each launch of a kernel family in the bit set `families`
+ * made by any later call records events[2 i] just before and events[2 i + 1]
+ * just after the launch on that call's stream, and (when fam_out is not NULL)
+ * writes the launch's family bit to fam_out[i], a HOST array, for
+ * i < capacity; further launches are not recorded.  `events` are
+ * caller-created HIP events (2 * capacity of them) that must outlive the
+ * recorded launches.  families = SHAMPOO_TIME_OFF disables the hook.  The hook
+ * is process-wide and not thread-safe; enabling it resets the count.
  * shampoo_timing_count returns how many launches have been recorded.
  */
-int shampoo_timing_hook(int family, hipEvent_t* events, int capacity);
+int shampoo_timing_hook(int families, hipEvent_t* events, int32_t* fam_out, int capacity);
 int shampoo_timing_count(void);
 
 #ifdef __cplusplus

@@ -27,6 +27,7 @@ NOALLOC_SCRATCH_BYTES = 1 << 20
 BLK_NONFINITE = 1
 BLK_ZERO = 2
 BLK_NONPOS_RQ = 4
+BLK_RESID_GROWTH = 8
 # Precision
 F32 = 0
 BF16_IN = 1
@@ -49,7 +50,7 @@ OP_CHEBY = 4
 OP_PRECONDITION = 5
 OP_GRAFT = 6
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class shampoo_block(ctypes.Structure):
@@ -70,12 +71,13 @@ class ShampooError(RuntimeError):
 TIME_OFF = 0
 TIME_NDB_PAIR = 1
 TIME_NDB_P = 2
-TIME_CLENSHAW = 3
-TIME_CN_M = 4
+TIME_CLENSHAW = 4
+TIME_CN_M = 8
+TIME_ALL = 15
 
 _SIGNATURES = {
     "shampoo_abi_version": (c_int, []),
-    "shampoo_timing_hook": (c_int, [c_int, c_void_p, c_int]),
+    "shampoo_timing_hook": (c_int, [c_int, c_void_p, c_void_p, c_int]),
     "shampoo_timing_count": (c_int, []),
     "shampoo_strerror": (ctypes.c_char_p, [c_int]),
     "shampoo_workspace_bytes": (c_size_t, [c_int, c_int64, c_int, c_int, c_int]),
@@ -170,8 +172,8 @@ def shampoo_precondition(x_roots, g_blocks, nblocks, B, u_blocks, prec, ws, ws_b
     return load().shampoo_precondition(x_roots, g_blocks, nblocks, B, u_blocks, prec, ws, ws_bytes, stream)
 
 
-def shampoo_timing_hook(family, events, capacity):
-    return load().shampoo_timing_hook(family, events, capacity)
+def shampoo_timing_hook(families, events, fam_out, capacity):
+    return load().shampoo_timing_hook(families, events, fam_out, capacity)
 
 
 def shampoo_timing_count():

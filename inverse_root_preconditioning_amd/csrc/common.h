@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <cfloat>
 #include <stdint.h>
 
 #include <type_traits>

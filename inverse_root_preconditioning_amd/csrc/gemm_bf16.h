@@ -87,10 +87,9 @@ struct H16Shape {
   static constexpr int MINW = CFG == H16_T256 ? 1 : 2;
 };
 
-// Symmetric products stay on 128 x 128 tiles: their diagonal tiles are
-// computed whole, which wastes more work on larger tiles, and their
-// epilogues (EMA and Clenshaw terms, mirrored writes) outweigh the main-loop
-// gain.
+// Output tile edge of the 16-bit products: 256 x 256 tiles whenever B is a
+// multiple of 256 (symmetric products too: their diagonal tiles skip the
+// 32 x 32 blocks that lie below the diagonal), 128 x 128 otherwise.
 __host__ __device__ constexpr int h16_tile_of(int B, bool sym) { return (B % 256 == 0) ? 256 : 128; }
 
 // C_i = A_i Bt_i^T for 16-bit (bf16 or fp16) row-major stacks, fp32 accumulate.

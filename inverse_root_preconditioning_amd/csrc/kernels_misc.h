@@ -24,21 +24,46 @@ __global__ void __launch_bounds__(256) trace_kernel(const float* __restrict__ F,
 }
 
 // ---------------------------------------------------------------------------
-// Frobenius norm: sum of squares in `chunks` slices per factor, then one wave
-// per factor finishes ||F + eps I||_F^2 = sum F^2 + 2 eps tr + B eps^2.
+// Range of the scale stage.  The power iteration and the Frobenius norm sum
+// squares of entries of size ~ the factor's eigenvalues, which leave fp32's
+// range for factors with entries beyond ~1e18 or below ~1e-19 although the
+// factor itself and every later step (which work on F / c) are fine there.
+// Both therefore work on F 2^-e, with 2^e the power of two just above the
+// mean eigenvalue |tr F| / B, and scale the result back by 2^e.  Scaling by a
+// power of two is exact, so inside the old range the results are unchanged.
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) sumsq_kernel(const float* __restrict__ F, int64_t per_factor,
-                                                    int chunks, float* __restrict__ partials) {
+__device__ __forceinline__ int range_exp(float trace, int B) {
+  const float m = fabsf(trace) / (float)B;
+  if (!(m >= FLT_MIN) || !(m <= FLT_MAX)) return 0;  // zero, subnormal, NaN or infinite trace
+  const int e = (int)((__float_as_uint(m) >> 23) & 0xff) - 126;  // m in [2^(e-1), 2^e)
+  return e < -125 ? -125 : (e > 125 ? 125 : e);
+}
+
+// 2^e for -126 <= e <= 127.
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(127 + e) << 23); }
+
+// ---------------------------------------------------------------------------
+// Frobenius norm: sum of squares of F 2^-e (range_exp) in `chunks` slices per
+// factor, then one wave per factor finishes
+// ||F + eps I||_F^2 2^-2e = sum (F 2^-e)^2 + 2 (eps 2^-e)(tr 2^-e) + B (eps 2^-e)^2.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) sumsq_kernel(const float* __restrict__ F, int B, int chunks,
+                                                    const shampoo_scale* __restrict__ sc,
+                                                    float* __restrict__ partials) {
   __shared__ float red[4];
   const int64_t f = blockIdx.x / chunks;
   const int chunk = blockIdx.x - (int)(f * chunks);
+  const int64_t per_factor = (int64_t)B * B;
   const int64_t n4 = per_factor / 4;
   const int64_t len = (n4 + chunks - 1) / chunks;
   const int64_t lo = chunk * len, hi = min(n4, lo + len);
   const floatx4* p = reinterpret_cast<const floatx4*>(F + f * per_factor);
+  const float r = pow2f(-range_exp(sc[f].trace, B));
   float s = 0.f;
   for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
-    const floatx4 v = p[i];
+    floatx4 v = p[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= r;
     s += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
   }
   const float t = block_sum<256>(s, red);
@@ -70,8 +95,10 @@ __global__ void __launch_bounds__(64) frob_finalize_kernel(const float* __restri
   s = wave_sum(s);
   if (threadIdx.x == 0) {
     const float tr = sc[f].trace, eps = sc[f].eps;
-    const float n2 = s + 2.f * eps * tr + (float)B * eps * eps;
-    const float lam = sqrtf(n2);
+    const int ex = range_exp(tr, B);
+    const float r = pow2f(-ex), trr = tr * r, epsr = eps * r;
+    const float n2 = s + 2.f * epsr * trr + (float)B * epsr * epsr;
+    const float lam = sqrtf(n2) * pow2f(ex);
     sc[f].lambda = lam;
     sc[f].c = lam;
     status[f] = scale_status(tr, lam);
@@ -216,12 +243,13 @@ __global__ void __launch_bounds__(256, 2) pi_step_kernel(const PiArgs P) {
   if (ks == 0) {
     const float sj = s_col[j];
     const float eps = P.sc[f].eps;
+    const float rinv = pow2f(-range_exp(P.sc[f].trace, P.B));
     float nsum = 0.f, rsum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = m0 + rb * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
       const float v = (j < P.r) ? ldg(vv.p + (int64_t)row * P.ldv + j) * sj : 0.f;
-      const float w = acc[e] * sj + eps * v;
+      const float w = (acc[e] * sj + eps * v) * rinv;
       if (!P.last) stg(P.wout + (f * P.B + row) * kPiCols + j, w);
       nsum += w * w;
       rsum += v * w;
@@ -350,12 +378,13 @@ __global__ void __launch_bounds__(256, 2) pi_step_dma_kernel(const PiArgs P) {
   const int j = lane & 31;
   const float sj = s_col[j];
   const float eps = P.sc[f].eps;
+    const float rinv = pow2f(-range_exp(P.sc[f].trace, P.B));
   float nsum = 0.f, rsum = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int row = m0 + wave * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
     const float v = (j < P.r) ? ldg(Vp + (int64_t)row * kPiCols + j) * sj : 0.f;
-    const float w = acc[e] * sj + eps * v;
+    const float w = (acc[e] * sj + eps * v) * rinv;
     if (!P.last) stg(P.wout + (f * B + row) * kPiCols + j, w);
     nsum += w * w;
     rsum += v * w;
@@ -480,12 +509,13 @@ __global__ void __launch_bounds__(512, 2) pi_step_col_kernel(const PiArgs P) {
   const int j = lane & 31;
   const float sj = s_col[j];
   const float eps = P.sc[f].eps;
+    const float rinv = pow2f(-range_exp(P.sc[f].trace, P.B));
   float nsum = 0.f, rsum = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
     const int row = m0 + wave * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
     const float v = (j < P.r) ? ldg(Vp + (int64_t)row * kPiCols + j) * sj : 0.f;
-    const float w = acc[e] * sj + eps * v;
+    const float w = (acc[e] * sj + eps * v) * rinv;
     if (!P.last) stg(P.wout + (f * B + row) * kPiCols + j, w);
     nsum += w * w;
     rsum += v * w;
@@ -511,8 +541,9 @@ __global__ void __launch_bounds__(512, 2) pi_step_col_kernel(const PiArgs P) {
   }
 }
 
-// One wave per factor: lambda = max_j q_j, c = safety lambda, status bits.
-__global__ void __launch_bounds__(64) pi_finalize_kernel(const float* __restrict__ rq, int npanels, int r,
+// One wave per factor: lambda = 2^e max_j q_j (the steps worked on F 2^-e, see
+// range_exp), c = safety lambda, status bits.
+__global__ void __launch_bounds__(64) pi_finalize_kernel(const float* __restrict__ rq, int npanels, int r, int B,
                                                         float safety, shampoo_scale* __restrict__ sc,
                                                         int32_t* __restrict__ status) {
   const int64_t f = blockIdx.x;
@@ -527,8 +558,8 @@ __global__ void __launch_bounds__(64) pi_finalize_kernel(const float* __restrict
   const float lam0 = wave_max(nan ? -INFINITY : q);
   const int any_nan = __any(nan);
   if (j == 0) {
-    const float lam = any_nan ? __int_as_float(0x7fc00000) : lam0;
     const float tr = sc[f].trace;
+    const float lam = any_nan ? __int_as_float(0x7fc00000) : lam0 * pow2f(range_exp(tr, B));
     sc[f].lambda = lam;
     sc[f].c = safety * lam;
     status[f] = scale_status(tr, lam);
@@ -713,8 +744,15 @@ __global__ void __launch_bounds__(256) cheby16_start_kernel(const Cheby16StartAr
 }
 
 // resid[f][col] = sqrt(sum of partials[f][:count]); NONFINITE if not finite.
+// Residual of one iteration per factor from the epilogue's per-tile partial
+// sums of squares (fixed order).  rmin[f] tracks the smallest residual of the
+// current pass (reset when `first`): a residual above twice it sets
+// RESID_GROWTH -- in exact arithmetic the residuals of a pass never increase
+// for spectra inside the convergence region, so such a rise is rounding
+// error being amplified.
 __global__ void __launch_bounds__(64) resid_kernel(const float* __restrict__ partials, int count,
                                                   float* __restrict__ resid, int ncols, int col,
+                                                  float* __restrict__ rmin, int first,
                                                   int32_t* __restrict__ status) {
   const int64_t f = blockIdx.x;
   float s = 0.f;
@@ -723,7 +761,13 @@ __global__ void __launch_bounds__(64) resid_kernel(const float* __restrict__ par
   if (threadIdx.x == 0) {
     const float r = sqrtf(s);
     if (resid != nullptr) resid[f * ncols + col] = r;
-    if (!isfinite(r) && status != nullptr && !degenerate(status[f])) status[f] |= SHAMPOO_BLK_NONFINITE;
+    const float lo = first ? r : rmin[f];
+    if (status != nullptr && !degenerate(status[f])) {
+      int bits = isfinite(r) ? 0 : SHAMPOO_BLK_NONFINITE;
+      if (!first && r > 2.f * lo) bits |= SHAMPOO_BLK_RESID_GROWTH;
+      if (bits) status[f] |= bits;
+    }
+    rmin[f] = fminf(lo, r);
   }
 }
 

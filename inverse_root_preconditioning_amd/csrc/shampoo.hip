@@ -29,14 +29,15 @@ int check_launch() { return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMP
 // Timing hook (shampoo_timing_hook): events recorded around launches of one
 // kernel family on the launch's own stream.
 struct TimingHook {
-  int family = 0;
+  int families = 0;
   hipEvent_t* events = nullptr;
+  int32_t* fam_out = nullptr;
   int capacity = 0;
   int count = 0;
 } g_timing;
 
 bool timing_on(int fam) {
-  return fam != 0 && g_timing.family == fam && g_timing.count < g_timing.capacity;
+  return (g_timing.families & fam) != 0 && g_timing.count < g_timing.capacity;
 }
 void timing_before(int fam, hipStream_t st) {
   if (timing_on(fam)) (void)hipEventRecord(g_timing.events[2 * g_timing.count], st);
@@ -44,6 +45,7 @@ void timing_before(int fam, hipStream_t st) {
 void timing_after(int fam, hipStream_t st) {
   if (timing_on(fam)) {
     (void)hipEventRecord(g_timing.events[2 * g_timing.count + 1], st);
+    if (g_timing.fam_out != nullptr) g_timing.fam_out[g_timing.count] = fam;
     ++g_timing.count;
   }
 }
@@ -185,9 +187,11 @@ int run_ew(const EwArgs& a, int64_t nf, hipStream_t st) {
   return check_launch();
 }
 
-int run_resid(const float* partials, int count, float* resid, int ncols, int col, int32_t* status, int64_t nf,
-              hipStream_t st) {
-  hipLaunchKernelGGL(resid_kernel, dim3((uint32_t)nf), dim3(64), 0, st, partials, count, resid, ncols, col, status);
+// `first`: the residual opens a pass (its running minimum restarts there).
+int run_resid(const float* partials, int count, float* resid, int ncols, int col, float* rmin, bool first,
+              int32_t* status, int64_t nf, hipStream_t st) {
+  hipLaunchKernelGGL(resid_kernel, dim3((uint32_t)nf), dim3(64), 0, st, partials, count, resid, ncols, col, rmin,
+                     first ? 1 : 0, status);
   return check_launch();
 }
 
@@ -222,6 +226,7 @@ struct Pool {
 struct NewtonWs {
   Pool pool;
   float* partials;
+  float* rmin;  // smallest residual of the current pass, per factor
 };
 
 // A pool of 16-bit stacks for the half-width coupled Newton.
@@ -247,6 +252,7 @@ struct Cn16Ws {
   Pool16 pool;
   float* c32;       // fp32 C_0 (one iteration only)
   float* partials;
+  float* rmin;      // smallest residual so far, per factor
 };
 
 size_t cn16_layout(Carver& c, int64_t nf, int B, Cn16Ws* out) {
@@ -259,6 +265,7 @@ size_t cn16_layout(Carver& c, int64_t nf, int B, Cn16Ws* out) {
   }
   const int cnt = gemm_tiles_max(B) > ew_chunks(B) ? gemm_tiles_max(B) : ew_chunks(B);
   w.partials = c.take<float>((size_t)nf * cnt);
+  w.rmin = c.take<float>((size_t)nf);
   if (out) *out = w;
   return c.off;
 }
@@ -274,6 +281,7 @@ size_t newton_layout(Carver& c, int64_t nf, int B, int variant, NewtonWs* out) {
   }
   const int cnt = gemm_tiles_max(B) > ew_chunks(B) ? gemm_tiles_max(B) : ew_chunks(B);
   w.partials = c.take<float>((size_t)nf * cnt);
+  w.rmin = c.take<float>((size_t)nf);
   if (out) *out = w;
   return c.off;
 }
@@ -461,7 +469,8 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
   a.B = B;
   a.chunks = ew_chunks(B);
   SHP_TRY(run_ew<EW_NDB_START>(a, nf, c.st));
-  SHP_TRY(run_resid(c.ws->partials, a.chunks, c.resid, c.ncols, pass * c.iters, c.status, nf, c.st));
+  SHP_TRY(run_resid(c.ws->partials, a.chunks, c.resid, c.ncols, pass * c.iters, c.ws->rmin, true, c.status, nf,
+                    c.st));
 
   const int tiles = f32_tiles<EpiNdbE>(B, c.sym_p);
   float* Z = E;  // Z_1 = E_0 (Z_0 = I)
@@ -530,7 +539,8 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
       const float* A[1] = {Z};
       const float* Bm[1] = {Y};
       SHP_TRY(gemm_nn<EpiNdbE>(A, Bm, &j, 1, nf, B, c.st, c.sym_p, SHAMPOO_TIME_NDB_P));
-      SHP_TRY(run_resid(c.ws->partials, tiles, c.resid, c.ncols, pass * c.iters + it, c.status, nf, c.st));
+      SHP_TRY(run_resid(c.ws->partials, tiles, c.resid, c.ncols, pass * c.iters + it, c.ws->rmin, false, c.status,
+                        nf, c.st));
     }
     const bool last = (it == c.iters - 1);
     if (!last) {
@@ -604,7 +614,7 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
   a.B = B;
   a.chunks = ew_chunks(B);
   SHP_TRY(run_ew<EW_CN_START>(a, nf, st));
-  SHP_TRY(run_resid(ws->partials, a.chunks, resid, iters, 0, status, nf, st));
+  SHP_TRY(run_resid(ws->partials, a.chunks, resid, iters, 0, ws->rmin, true, status, nf, st));
   const float pexp = -1.f / (float)p;
   if (iters == 1) {
     EwArgs s;
@@ -690,7 +700,7 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
       const float* A[1] = {Cp};
       const float* Bm[1] = {M};
       SHP_TRY(gemm_nn<EpiCnM>(A, Bm, &j, 1, nf, B, st, sym_c, SHAMPOO_TIME_CN_M));
-      SHP_TRY(run_resid(ws->partials, tiles, resid, iters, it + 1, status, nf, st));
+      SHP_TRY(run_resid(ws->partials, tiles, resid, iters, it + 1, ws->rmin, false, status, nf, st));
     }
     if (Cp != C) pool.put(Cp);
     pool.put(M);
@@ -727,7 +737,7 @@ int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int 
     a.B = B;
     a.chunks = ew_chunks(B);
     SHP_TRY(run_ew<EW_CN_START>(a, nf, st));
-    SHP_TRY(run_resid(ws->partials, a.chunks, resid, 1, 0, status, nf, st));
+    SHP_TRY(run_resid(ws->partials, a.chunks, resid, 1, 0, ws->rmin, true, status, nf, st));
     EwArgs s2;
     memset(&s2, 0, sizeof(s2));
     s2.x = ws->c32;
@@ -759,7 +769,7 @@ int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int 
     a.B = B;
     a.chunks = ew_chunks(B);
     SHP_TRY(run_ew<EW_CN16_START>(a, nf, st));
-    SHP_TRY(run_resid(ws->partials, a.chunks, resid, iters, 0, status, nf, st));
+    SHP_TRY(run_resid(ws->partials, a.chunks, resid, iters, 0, ws->rmin, true, status, nf, st));
   }
   const int tiles = (B / h16_tile_of(B, sym_c)) * (B / h16_tile_of(B, sym_c));  // reduction partials of C^p M
   uint16_t* X = nullptr;
@@ -828,7 +838,7 @@ int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int 
       const int rc = h16_gemm_nt<EpiCnM>(A, Bt, &j, 1, nf, B, sym_c, H16_F16, st);
       timing_after(SHAMPOO_TIME_CN_M, st);
       SHP_TRY(rc);
-      SHP_TRY(run_resid(ws->partials, tiles, resid, iters, it + 1, status, nf, st));
+      SHP_TRY(run_resid(ws->partials, tiles, resid, iters, it + 1, ws->rmin, false, status, nf, st));
     }
     if (Cp != C) pool.put(Cp);
     pool.put(M);
@@ -955,12 +965,13 @@ extern "C" {
 
 int shampoo_abi_version(void) { return SHAMPOO_ABI_VERSION; }
 
-int shampoo_timing_hook(int family, hipEvent_t* events, int capacity) {
-  if (family < 0 || family > SHAMPOO_TIME_CN_M || capacity < 0) return SHAMPOO_EINVAL;
-  if (family != 0 && (events == nullptr || capacity == 0)) return SHAMPOO_EINVAL;
-  g_timing.family = family;
-  g_timing.events = family ? events : nullptr;
-  g_timing.capacity = family ? capacity : 0;
+int shampoo_timing_hook(int families, hipEvent_t* events, int32_t* fam_out, int capacity) {
+  if ((families & ~SHAMPOO_TIME_ALL) != 0 || capacity < 0) return SHAMPOO_EINVAL;
+  if (families != 0 && (events == nullptr || capacity == 0)) return SHAMPOO_EINVAL;
+  g_timing.families = families;
+  g_timing.events = families ? events : nullptr;
+  g_timing.fam_out = families ? fam_out : nullptr;
+  g_timing.capacity = families ? capacity : 0;
   g_timing.count = 0;
   return SHAMPOO_OK;
 }
@@ -1068,8 +1079,8 @@ int shampoo_scale_power(const float* factors, int64_t nfactors, int B, float eps
   SHP_TRY(check_launch());
   if (mode == SHAMPOO_SCALE_FROBENIUS) {
     const int chunks = ew_chunks(B);
-    hipLaunchKernelGGL(sumsq_kernel, dim3((uint32_t)(nfactors * chunks)), dim3(256), 0, stream, factors,
-                       (int64_t)B * B, chunks, w.sumsq);
+    hipLaunchKernelGGL(sumsq_kernel, dim3((uint32_t)(nfactors * chunks)), dim3(256), 0, stream, factors, B, chunks,
+                       scale_out, w.sumsq);
     SHP_TRY(check_launch());
     hipLaunchKernelGGL(frob_finalize_kernel, dim3((uint32_t)nfactors), dim3(64), 0, stream, w.sumsq, chunks, B,
                        scale_out, status);
@@ -1106,8 +1117,8 @@ int shampoo_scale_power(const float* factors, int64_t nfactors, int B, float eps
       hipLaunchKernelGGL(pi_step_kernel<64>, dim3(P.total), dim3(256), 0, stream, P);
     SHP_TRY(check_launch());
   }
-  hipLaunchKernelGGL(pi_finalize_kernel, dim3((uint32_t)nfactors), dim3(64), 0, stream, w.rq, P.npanels, r, safety,
-                     scale_out, status);
+  hipLaunchKernelGGL(pi_finalize_kernel, dim3((uint32_t)nfactors), dim3(64), 0, stream, w.rq, P.npanels, r, B,
+                     safety, scale_out, status);
   return check_launch();
 }
 

@@ -251,6 +251,29 @@ class ShampooBlocks:
             raise ValueError("update_every must be >= 1")
         self.t = 0
 
+    def state_dict(self):
+        """The optimizer state needed to resume bit for bit: the EMA factors,
+        the cached roots with their scale records and status, and the step
+        count.  Tensors are returned as they are (device tensors); save them
+        with torch.save and load with torch.load(..., weights_only=True).
+        The power-iteration start vectors are the caller's input and are set
+        again with set_start_vectors after a restore."""
+        return {"factors": self.factors, "roots": self.roots, "scale": self.scale, "status": self.status,
+                "t": int(self.t), "B": int(self.cfg.B), "nblocks": int(self.nblocks)}
+
+    def load_state_dict(self, sd):
+        """Restore a state_dict() of a ShampooBlocks with the same B and block count."""
+        if int(sd["B"]) != self.cfg.B or int(sd["nblocks"]) != self.nblocks:
+            raise ValueError("state was saved for a different block size or block count")
+        for name in ("factors", "roots", "scale", "status"):
+            dst = getattr(self, name)
+            src = sd[name]
+            if tuple(src.shape) != tuple(dst.shape) or src.dtype != dst.dtype:
+                raise ValueError(f"{name}: saved {tuple(src.shape)} {src.dtype}, expected "
+                                 f"{tuple(dst.shape)} {dst.dtype}")
+            dst.copy_(src)
+        self.t = int(sd["t"])
+
     def set_start_vectors(self, v0):
         _check_f32_cuda(v0, "v0", (2 * self.nblocks, self.cfg.B, v0.shape[2]))
         self.v0 = v0

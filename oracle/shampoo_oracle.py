@@ -27,9 +27,11 @@ Readings taken where the pages leave a step open are listed with each
 function; the full list is in the design notes of the repository.
 
 Status bits (per factor) mirror the ones the library reports:
-  NONFINITE = 1   a non-finite trace or eigenvalue estimate
-  ZERO      = 2   trace of the factor is 0 (an all-zero history): X = I
-  NONPOS_RQ = 4   the spectral estimate is <= 0: X = I
+  NONFINITE    = 1   a non-finite trace or eigenvalue estimate
+  ZERO         = 2   trace of the factor is 0 (an all-zero history): X = I
+  NONPOS_RQ    = 4   the spectral estimate is <= 0: X = I
+  RESID_GROWTH = 8   a Newton residual rose above twice the smallest earlier
+                     one of its pass (see residual_growth)
 """
 from __future__ import annotations
 
@@ -40,6 +42,7 @@ import numpy as np
 NONFINITE = 1
 ZERO = 2
 NONPOS_RQ = 4
+RESID_GROWTH = 8
 
 F64 = np.float64
 
@@ -402,6 +405,31 @@ def graft_update(theta, m, v, g, U, lr, beta1, beta2, eps, step):
     nu = math.sqrt(float(np.sum(U * U)))
     s = math.sqrt(float(np.sum(P * P))) / nu if nu > 0.0 else 0.0
     return _f64(theta) - lr * s * U, m, v, s
+
+
+def residual_growth(residuals, per_pass, factor=2.0):
+    """Whether a residual list shows growth: some residual of a pass exceeds
+    `factor` times the smallest residual before it in the same pass.
+
+    The pages report that some low-precision Newton iterations are unstable
+    ([DASH] "Limitations": Newton-DB in FP16, coupled Newton in BF16;
+    "Scoreboard with context": Frobenius-scaled Newton-DB at B = 2048) but
+    give no detector.  Reading: in exact arithmetic ||I - Z Y||_F and
+    ||I - M||_F never increase within a pass for spectra inside the
+    convergence region (each eigenvalue's distance from 1 shrinks at every
+    iteration), so a rise above twice an earlier value means rounding errors
+    are being amplified.  `residuals` lists the passes one after another,
+    `per_pass` entries each; non-finite entries compare like any other value
+    (an infinite residual counts as growth, NaN never does).
+    """
+    res = [float(r) for r in residuals]
+    for start in range(0, len(res), per_pass):
+        lo = math.inf
+        for r in res[start:start + per_pass]:
+            if r > factor * lo:
+                return True
+            lo = min(lo, r)
+    return False
 
 
 def relative_frobenius(x, ref):

@@ -126,6 +126,43 @@ def test_residual_fourth_closed_forms():
     assert abs(O.residual_fourth(X, A) - 15.0 / 16.0) <= 1e-14
 
 
+def test_residual_growth_rule():
+    # hand-made residual lists: a fall then a rise above twice the minimum
+    assert O.residual_growth([5.0, 3.0, 7.0], 3)
+    assert not O.residual_growth([5.0, 3.0, 6.0], 3)          # exactly twice is not growth
+    assert not O.residual_growth([5.0, 4.0, 3.0, 3.3], 4)     # a small rise at the floor
+    assert O.residual_growth([1.0, 2.5], 2)                   # growth from the start
+    assert O.residual_growth([4.0, 1.0, math.inf], 3)
+    assert not O.residual_growth([4.0, 1.0, math.nan], 3)
+    # passes are judged separately: the second pass may start above the first pass's minimum
+    assert not O.residual_growth([5.0, 1.0, 3.0, 2.0], 2)
+    assert O.residual_growth([5.0, 1.0, 3.0, 7.0], 2)
+
+
+def test_float64_iterations_never_show_growth():
+    """In float64 the residuals of every solver fall monotonically (down to the
+    rounding floor, ~1e-14 here) on a spectrum spanning 1e-8..1 (the
+    ill-conditioned stress inputs), also for 20 iterations per pass."""
+    A, _, _ = rand_spd(10, 40, 1e8)
+    A_s = A / (2 * np.linalg.eigvalsh(A).max())
+    for chaining in ("Y", "Z"):
+        _, res = O.invroot_newton_db(A_s, 20, chaining)
+        assert not O.residual_growth(res, 20)
+        for r in (res[:20], res[20:]):  # non-increasing down to the float64 rounding floor
+            assert all(b <= a * (1 + 1e-12) + 1e-12 for a, b in zip(r, r[1:]))
+    _, res = O.coupled_newton(A_s, 4, 20)
+    assert not O.residual_growth(res, 20)
+    assert all(b <= a * (1 + 1e-12) + 1e-12 for a, b in zip(res, res[1:]))
+
+
+def test_growth_flags_a_spectrum_outside_the_convergence_region():
+    """Newton-DB on an eigenvalue of 7 (outside its region (0, 3)): z y goes
+    7 -> 28 -> 28 * 12.5^2 -> ... and the residual grows from the first step."""
+    _, _, res = O.newton_db_pass(np.diag([0.5, 7.0]), 4)
+    assert O.residual_growth(res, 4)
+    assert res[1] > 2 * res[0]
+
+
 # ---------------------------------------------------------------------------
 # Newton-DB
 # ---------------------------------------------------------------------------

@@ -121,6 +121,33 @@ def test_scale_power_matches_oracle(B, r):
     report("scale_power", B=B, r=r, err=err)
 
 
+@pytest.mark.parametrize("mode", [capi.SCALE_POWER, capi.SCALE_FROBENIUS])
+@pytest.mark.parametrize("mag", [1e30, 1e-30])
+def test_scale_and_roots_far_from_unit_magnitude(mode, mag):
+    """Factors with eigenvalues up to 1e30 (or down to 1e-33): the squares the
+    power iteration and the Frobenius norm form would leave fp32's range, so
+    the scale stage works on F 2^-e with 2^e near the mean eigenvalue; c, the
+    estimate and the roots still match the oracle, with no status bit."""
+    nf, B = 4, 256
+    F = (W.spd_factors(220, nf, B, cond=1e3).astype(np.float64) * mag).astype(np.float32)
+    V0 = W.start_vectors(221, nf, B)
+    Fd = dev(F)
+    # eps_rel = 1e-6 keeps eps a normal fp32 number at both magnitudes
+    sc, st = gpu_scale(Fd, 1e-6, mode, dev(V0), 20, 2.0)
+    X, _ = gpu_roots(Fd, sc, st, "newton", iters=6, p=4, variant=capi.NDB_Z)
+    s, stt, Xh = host(sc), host(st), host(X)
+    err = 0.0
+    for i in range(nf):
+        o = oracle_scale(F[i], 1e-6, mode, V0[i])
+        assert stt[i] == o["status"] == 0, (i, stt[i])
+        for k, key in enumerate(("c", "eps", "lam", "trace")):
+            e = abs(s[i, k] - o[key]) / abs(o[key])
+            assert e <= 2e-5, (key, s[i, k], o[key])
+        err = max(err, O.relative_frobenius(Xh[i], oracle_root(F[i], o, "newton", iters=6, variant=capi.NDB_Z)))
+    assert err <= TOL_F32, err
+    report("scale_range", mode=mode, mag=mag, root_err=err)
+
+
 def test_scale_frobenius_matches_oracle():
     nf, B = 5, 128
     F = W.spd_factors(20, nf, B, cond=1e2)
@@ -221,6 +248,88 @@ def test_newton_db_residuals_match_oracle():
         A_s = O.damped(F[i], o["eps"]) / o["c"]
         _, res = O.invroot_newton_db(A_s, k, "Y")
         assert np.allclose(Rh[i], res, rtol=1e-3, atol=1e-5), (Rh[i], res)
+
+
+_RESID_CACHE = {}
+
+
+def _oracle_residuals(B, variant, iters):
+    """(F, V0, per-factor oracle residual lists) for the large-kernel residual tests."""
+    key = (B, variant, iters)
+    if key not in _RESID_CACHE:
+        nf = 2
+        F = W.spd_factors(200 + B, nf, B, cond=1e3)
+        V0 = W.start_vectors(201, nf, B)
+        refs = []
+        for i in range(nf):
+            o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
+            A_s = O.damped(F[i], o["eps"]) / o["c"]
+            if variant in (capi.CN, capi.CN_F16):
+                refs.append(O.coupled_newton(A_s, 4, iters)[1])
+            else:
+                refs.append(O.invroot_newton_db(A_s, iters, "Z" if variant == capi.NDB_Z else "Y")[1])
+        _RESID_CACHE[key] = (F, V0, np.array(refs))
+    return _RESID_CACHE[key]
+
+
+@pytest.mark.parametrize("mode", ["sym", "full", "sym_coupling"])
+@pytest.mark.parametrize("variant", [capi.NDB, capi.NDB_Z, capi.CN])
+@pytest.mark.parametrize("B", [512, 1024])
+def test_residuals_match_oracle_large_kernel(B, variant, mode):
+    """The per-iteration residuals (||I - Z Y||_F of both Newton-DB passes,
+    ||I - M||_F of coupled Newton) that the 256 x 256 fp32 kernel's epilogue
+    reduces, against the float64 iteration's: with the coupling product in
+    full (default), every product in full, and the coupling product from upper
+    tiles (diagonal tiles' upper entries weighted twice).  Above the fp32
+    rounding floor the residuals agree to 1e-3 relative; at the floor (about
+    1e-4 here) the computed value measures rounding, and is bounded by 1e-3."""
+    iters = 6
+    F, V0, ref = _oracle_residuals(B, variant, iters)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    bits = {"sym": 0, "full": capi.FULL_PRODUCTS, "sym_coupling": capi.SYM_COUPLING}[mode]
+    _, R = gpu_roots(Fd, sc, st, "newton", iters=iters, p=4, variant=variant | bits, resid=True)
+    Rh, sth = host(R), host(st)
+    assert Rh.shape == ref.shape
+    live = ref > 1e-2
+    rel = np.abs(Rh - ref) / np.where(live, ref, 1.0)
+    assert np.all(rel[live] <= 1e-3), (Rh, ref)
+    assert np.all(np.abs(Rh - ref)[~live] <= 1e-3), (Rh, ref)
+    assert np.all(sth == 0)
+    report("resid_large_kernel", B=B, variant=variant, mode=mode, max_rel=float(rel[live].max()),
+           floor_max=float(np.abs(Rh - ref)[~live].max()) if (~live).any() else 0.0)
+
+
+@pytest.mark.parametrize("B", [512, 1024])
+def test_residuals_match_oracle_fp16_coupled_newton(B):
+    """||I - M||_F from the epilogue of the fp16-operand C^p M product against
+    the float64 coupled Newton: within the half-width bar, 2e-2 relative, while
+    above fp16's rounding floor (bounded by 0.5 there)."""
+    iters = 6
+    F, V0, ref = _oracle_residuals(B, capi.CN_F16, iters)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    _, R = gpu_roots(Fd, sc, st, "newton", iters=iters, p=4, variant=capi.CN_F16, resid=True)
+    Rh = host(R)
+    live = ref > 1.0
+    rel = np.abs(Rh - ref) / np.where(live, ref, 1.0)
+    assert np.all(rel[live] <= TOL_BF16), (Rh, ref)
+    assert np.all(np.abs(Rh - ref)[~live] <= 0.5), (Rh, ref)
+    report("resid_cn_fp16", B=B, max_rel=float(rel[live].max()))
+
+
+def test_binding_rejects_short_residual_and_status_tensors():
+    nf, B = 2, 64
+    F = dev(W.spd_factors(210, nf, B, cond=10.0))
+    sc, st = PL.new_scale(nf, "cuda")
+    X = torch.empty_like(F)
+    short = torch.zeros((nf, 5), dtype=torch.float32, device="cuda")  # one pass of 5; Newton-DB p = 4 needs 10
+    with pytest.raises(ValueError, match="resid_out"):
+        PL.invroot_newton(F, sc, 4, capi.NDB, 5, X, st, short)
+    with pytest.raises(ValueError, match="status"):
+        PL.invroot_newton(F, sc, 4, capi.NDB, 5, X, st.to(torch.int64))
+    with pytest.raises(ValueError, match="scale"):
+        PL.invroot_cheby(F, sc[:1], 4, 8, 0.0, capi.F32, X, st)
 
 
 @pytest.mark.parametrize("full", [False, True])
