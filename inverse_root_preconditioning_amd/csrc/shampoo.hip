@@ -22,8 +22,6 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool valid_B(int B) { return B >= 64 && B <= kMaxB && (B % 64) == 0; }
 
-int tile_of(int B) { return (B % 128 == 0) ? 128 : 64; }
-
 int check_launch() { return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMPOO_EHIP; }
 
 // Timing hook (shampoo_timing_hook): events recorded around launches of one
@@ -73,25 +71,37 @@ int ew_chunks(int B) {
   return (int)c;
 }
 
-// Output tile edge of an fp32 product: gemm_f32_big_kernel (256) for dense
-// operands when B is a multiple of 256 and the epilogue fits that kernel's
-// register budget, else 128 or 64.
+// Output tile edge of an fp32 launch covering `items` products (jobs x
+// factors): gemm_f32_big_kernel's 256 x 256 tiles for dense operands when B is
+// a multiple of 256 and the epilogue fits that kernel's register budget, else
+// gemm_f32_kernel's 128 x 128 (B a multiple of 128) or 64 x 64 tiles -- the
+// largest of these whose grid still gives every compute unit a workgroup,
+// and the 64 x 64 tiles when none does (a small batch is bound by how many
+// compute units it occupies, not by the per-tile efficiency of larger tiles).
+constexpr int64_t kComputeUnits = 256;
+
 template <class Epi>
-int f32_tile_edge(int B, bool sym, bool dense) {
+int f32_tile_edge(int B, bool sym, bool dense, int64_t items) {
+  auto grid = [&](int T) {
+    const int64_t t = B / T;
+    return items * (sym ? t * (t + 1) / 2 : t * t);
+  };
   const bool fits = sym ? Epi::kBigSym : Epi::kBigFull;
-  return (dense && fits && B % kBigTile == 0) ? kBigTile : tile_of(B);
+  if (dense && fits && B % kBigTile == 0 && grid(kBigTile) >= kComputeUnits) return kBigTile;
+  if (B % 128 == 0 && grid(128) >= kComputeUnits) return 128;
+  return 64;
 }
 
 // Tile count (reduction partials per item) of a product of dense stacks.
 template <class Epi>
-int f32_tiles(int B, bool sym) {
-  const int t = B / f32_tile_edge<Epi>(B, sym, true);
+int f32_tiles(int B, bool sym, int64_t items) {
+  const int t = B / f32_tile_edge<Epi>(B, sym, true, items);
   return t * t;
 }
 
 // The most tiles any fp32 product of size B uses (workspace sizing).
 int gemm_tiles_max(int B) {
-  const int t = B / tile_of(B);
+  const int t = B / 64;
   return t * t;
 }
 
@@ -109,7 +119,7 @@ int run_gemm(const Operand* a, const Operand* b, const typename Epi::Job* e, int
     P.b[j] = b[j];
     P.e[j] = e[j];
   }
-  const int T = f32_tile_edge<Epi>(B, sym, LA == KCONTIG && LB == MNCONTIG && !DA && !DB);
+  const int T = f32_tile_edge<Epi>(B, sym, LA == KCONTIG && LB == MNCONTIG && !DA && !DB, (int64_t)njobs * nitems);
   const bool big = T == kBigTile;
   P.nitems = nitems;
   P.B = B;
@@ -472,7 +482,7 @@ int ndb_pass(const NdbCtx& c, const float* src, bool y0_in_src, const shampoo_sc
   SHP_TRY(run_resid(c.ws->partials, a.chunks, c.resid, c.ncols, pass * c.iters, c.ws->rmin, true, c.status, nf,
                     c.st));
 
-  const int tiles = f32_tiles<EpiNdbE>(B, c.sym_p);
+  const int tiles = f32_tiles<EpiNdbE>(B, c.sym_p, nf);
   float* Z = E;  // Z_1 = E_0 (Z_0 = I)
   // Iteration 1: Y_1 = Y_0 E_0.
   if (c.iters == 1) {
@@ -630,7 +640,7 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
     s.chunks = ew_chunks(B);
     return run_ew<EW_SCALE_COPY>(s, nf, st);
   }
-  const int tiles = f32_tiles<EpiCnM>(B, sym_c);
+  const int tiles = f32_tiles<EpiCnM>(B, sym_c, nf);
   float* X = nullptr;  // X_1 = C_0 (X_0 = I): first iteration has no X product
   for (int it = 0; it < iters; ++it) {
     const bool last = (it == iters - 1);

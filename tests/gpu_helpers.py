@@ -73,3 +73,17 @@ def oracle_root(F, sc, method, iters=10, p=4, variant=capi.NDB, degree=24, delta
     if method == "newton":
         return O.invroot(F, sc, VARIANT_NAME[variant], iters=iters, p=p, chaining=CHAINING[variant])
     return O.invroot(F, sc, "cheby", p=p, degree=degree, delta=delta)
+
+
+def fill_factor(B, per_factor_tiles, base, cus=256):
+    """How many copies of `base` checked factors a stack needs so that a launch
+    over it has at least `cus` workgroups of `per_factor_tiles` tiles per
+    factor: below that, the library picks smaller tiles to fill the GPU, so
+    tests meant for the large-tile kernels replicate their factors."""
+    need = -(-cus // per_factor_tiles)
+    return -(-need // base)
+
+
+def upper_tiles(B, T):
+    t = B // T
+    return t * (t + 1) // 2

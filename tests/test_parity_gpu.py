@@ -13,8 +13,8 @@ from inverse_root_preconditioning_amd import capi
 from inverse_root_preconditioning_amd import pipeline as PL
 from inverse_root_preconditioning_amd import workloads as W
 
-from gpu_helpers import (TOL_BF16, TOL_F32, dev, gpu_roots, gpu_scale, host, oracle_root, oracle_scale,
-                         report)
+from gpu_helpers import (TOL_BF16, TOL_F32, dev, fill_factor, gpu_roots, gpu_scale, host, oracle_root,
+                         oracle_scale, report, upper_tiles)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,21 +36,23 @@ def grads(key, n, B, std=1.0):
 # accumulate
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("B", [64, 128, 192, 256])
-def test_accumulate_gram_matches_oracle(B):
-    n = 3
+@pytest.mark.parametrize("B,n", [(64, 3), (128, 3), (192, 3), (256, 3), (256, 86)])
+def test_accumulate_gram_matches_oracle(B, n):
+    """n = 86 blocks of 256 fill the GPU with 128 x 128 tiles (3 upper tiles
+    each), the descriptor kernel the model-shaped steps run; fewer blocks run
+    64 x 64 tiles.  The first three blocks are checked."""
     G = grads(1, n, B, 0.02)
     g = dev(G)
     table = PL.BlockTable.from_stack(g)
     F = torch.zeros((2 * n, B, B), dtype=torch.float32, device="cuda")
     PL.accumulate(table, F, 0.0, 1.0)
     out = host(F)
-    for i in range(n):
+    for i in range(3):
         L, R = O.accumulate(np.zeros((B, B)), np.zeros((B, B)), G[i], 0.0, 1.0)
         el, er = O.relative_frobenius(out[i], L), O.relative_frobenius(out[n + i], R)
         assert el <= 1e-5 and er <= 1e-5, (el, er)
         assert np.array_equal(out[i], out[i].T) and np.array_equal(out[n + i], out[n + i].T)
-    report("accumulate_gram", B=B, err=max(el, er))
+    report("accumulate_gram", B=B, n=n, err=max(el, er))
 
 
 def test_accumulate_ema_ragged_blocks():
@@ -208,10 +210,15 @@ def test_fp32_products_span_tiles(B, solver, variant, arg, full):
     B = 768 on 3 x 3 and B = 1280 on 5 x 5 (15 upper tiles; the coupled-Newton
     C^p M product with its epilogue through LDS), B = 640 the 128 x 128 kernel
     on 5 x 5 tiles; symmetric and full products, reductions and epilogues all
-    cross tile boundaries."""
-    nf = 3
-    F = W.spd_factors(70 + B, nf, B, cond=1e3)
-    V0 = W.start_vectors(71, nf, B)
+    cross tile boundaries.  The three checked factors are replicated until a
+    symmetric product's grid fills the GPU (below that the library picks
+    smaller tiles); every copy must give the same bits."""
+    base = 3
+    T = 256 if B % 256 == 0 else 128
+    reps = fill_factor(B, upper_tiles(B, T), base)
+    nf = base * reps
+    F = np.concatenate([W.spd_factors(70 + B, base, B, cond=1e3)] * reps)
+    V0 = np.concatenate([W.start_vectors(71, base, B)] * reps)
     Fd = dev(F)
     sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
     if solver == "newton":
@@ -221,8 +228,9 @@ def test_fp32_products_span_tiles(B, solver, variant, arg, full):
     else:
         X, _ = gpu_roots(Fd, sc, st, "cheby", degree=arg, prec=capi.F32)
     Xh = host(X)
+    assert all(np.array_equal(Xh[i], Xh[i % base]) for i in range(nf))
     err = 0.0
-    for i in range(nf):
+    for i in range(base):
         o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
         if solver == "newton":
             ref = oracle_root(F[i], o, "newton", iters=arg, p=4, variant=variant)
@@ -231,8 +239,8 @@ def test_fp32_products_span_tiles(B, solver, variant, arg, full):
         err = max(err, O.relative_frobenius(Xh[i], ref))
     assert err <= TOL_F32, err
     if not full and variant != capi.CN:
-        assert all(np.array_equal(Xh[i], Xh[i].T) for i in range(nf))
-    report("fp32_span_tiles", B=B, solver=solver, variant=variant, arg=arg, full=full, err=err)
+        assert all(np.array_equal(Xh[i], Xh[i].T) for i in range(base))
+    report("fp32_span_tiles", B=B, solver=solver, variant=variant, arg=arg, full=full, nf=nf, err=err)
 
 
 def test_newton_db_residuals_match_oracle():
@@ -285,11 +293,14 @@ def test_residuals_match_oracle_large_kernel(B, variant, mode):
     1e-4 here) the computed value measures rounding, and is bounded by 1e-3."""
     iters = 6
     F, V0, ref = _oracle_residuals(B, variant, iters)
-    Fd = dev(F)
-    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    reps = fill_factor(B, upper_tiles(B, 256), F.shape[0])  # the 256 x 256 kernel, as the model-shaped steps
+    Fd = dev(np.concatenate([F] * reps))
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(np.concatenate([V0] * reps)))
     bits = {"sym": 0, "full": capi.FULL_PRODUCTS, "sym_coupling": capi.SYM_COUPLING}[mode]
     _, R = gpu_roots(Fd, sc, st, "newton", iters=iters, p=4, variant=variant | bits, resid=True)
     Rh, sth = host(R), host(st)
+    assert all(np.array_equal(Rh[i], Rh[i % F.shape[0]]) for i in range(Rh.shape[0]))
+    Rh = Rh[:F.shape[0]]
     assert Rh.shape == ref.shape
     live = ref > 1e-2
     rel = np.abs(Rh - ref) / np.where(live, ref, 1.0)
@@ -457,9 +468,10 @@ def test_repeat_runs_are_bitwise_identical_large_tiles():
     """The same on 2 x 2 large tiles: power iteration by columns, Newton-DB on
     the fp32 large kernel and bf16 Chebyshev on the 8-wave 16-bit kernel with
     their LDS-staged symmetric epilogues (fixed reduction orders throughout)."""
-    nf, B = 3, 512
-    F = W.spd_factors(92, nf, B, cond=1e4)
-    V0 = W.start_vectors(93, nf, B)
+    B = 512
+    reps = fill_factor(B, upper_tiles(B, 256), 3)
+    F = np.concatenate([W.spd_factors(92, 3, B, cond=1e4)] * reps)
+    V0 = np.concatenate([W.start_vectors(93, 3, B)] * reps)
     Fd, Vd = dev(F), dev(V0)
     outs = []
     for _ in range(2):
@@ -556,13 +568,14 @@ def test_symmetric_coupling_opt_in(B, variant, iters, tol):
     symmetric.  B = 768 runs Z Y on 3 x 3 tiles of the large kernel (three
     diagonal tiles, reductions standing for mirrored tiles)."""
     nf = 4
-    F = W.spd_factors(160, nf, B, cond=1e3)
-    V0 = W.start_vectors(161, nf, B)
+    reps = fill_factor(B, upper_tiles(B, 256), nf) if B >= 512 else 1
+    F = np.concatenate([W.spd_factors(160, nf, B, cond=1e3)] * reps)
+    V0 = np.concatenate([W.start_vectors(161, nf, B)] * reps)
     Fd = dev(F)
     sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
     X, R = gpu_roots(Fd, sc, st, "newton", iters=iters, p=4, variant=variant | capi.SYM_COUPLING, resid=True)
     _, R0 = gpu_roots(Fd, sc, st, "newton", iters=iters, p=4, variant=variant, resid=True)
-    Xh, Rh, R0h = host(X), host(R), host(R0)
+    Xh, Rh, R0h = host(X)[:nf], host(R)[:nf], host(R0)[:nf]
     base = capi.CN if variant == capi.CN_F16 else variant
     err = 0.0
     for i in range(nf):
