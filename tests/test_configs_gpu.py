@@ -260,10 +260,14 @@ def model_step(cfg_id, spec, B, method, variant=capi.NDB, prec=capi.F32, degree=
     return grads, layout, V0, state, outs
 
 
-def sampled_parity(cfg_id, grads, layout, V0, state, outs, B, method, variant, degree, iters):
+def sampled_parity(cfg_id, grads, layout, V0, state, outs, B, method, variant, degree, iters, count=13):
+    """Blocks 0, 1 and the last plus `count` drawn with seed (config, subset):
+    16 blocks by default.  Returns (picks, max factor error, max root error,
+    max U error, per-block root and U errors)."""
     n = len(layout)
-    picks = W.sampled_blocks(cfg_id, n)
+    picks = W.sampled_blocks(cfg_id, n, count=count)
     ef = ex = eu = 0.0
+    per_x, per_u = [], []
     for i in picks:
         br = layout[i]
         g = O.pad_block(grads[br.weight][br.row0:br.row0 + br.rows, br.col0:br.col0 + br.cols], B)
@@ -276,12 +280,16 @@ def sampled_parity(cfg_id, grads, layout, V0, state, outs, B, method, variant, d
                 xo = oracle_root(Fo, so, "newton", iters=iters, variant=variant)
             else:
                 xo = oracle_root(Fo, so, "cheby", degree=degree, delta=1e-12)
-            ex = max(ex, O.relative_frobenius(host(state.roots[j]), xo))
+            e = O.relative_frobenius(host(state.roots[j]), xo)
+            ex = max(ex, e)
+            per_x.append(e)
             xs.append(xo)
         uo = O.precondition(xs[0], g, xs[1])
         ug = host(outs[br.weight][br.row0:br.row0 + br.rows, br.col0:br.col0 + br.cols])
-        eu = max(eu, O.relative_frobenius(ug, uo[:br.rows, :br.cols]))
-    return picks, ef, ex, eu
+        e = O.relative_frobenius(ug, uo[:br.rows, :br.cols])
+        eu = max(eu, e)
+        per_u.append(e)
+    return picks, ef, ex, eu, (per_x, per_u)
 
 
 @pytest.mark.slow
@@ -289,8 +297,9 @@ def sampled_parity(cfg_id, grads, layout, V0, state, outs, B, method, variant, d
 def test_config3_sampled(variant):
     B = 1024
     run = model_step(3, W.MODEL_360M, B, "newton", variant=variant)
-    picks, ef, ex, eu = sampled_parity(3, *run, B, "newton", variant, 24, 10)
-    report("config3", variant=variant, blocks=picks, factor_err=ef, root_err=ex, U_err=eu)
+    picks, ef, ex, eu, (px, pu) = sampled_parity(3, *run, B, "newton", variant, 24, 10)
+    report("config3", variant=variant, blocks=picks, factor_err=ef, root_err=ex, U_err=eu,
+           root_err_median=float(np.median(px)), U_err_median=float(np.median(pu)))
     assert ef <= 1e-5
     if variant == capi.NDB_Z:
         assert ex <= TOL_F32 and eu <= TOL_F32
@@ -302,7 +311,7 @@ def test_config3_sampled_symmetric_coupling():
     360M-shaped step with Newton-DB k = 10, Z-chained, as the benchmark runs it."""
     B = 1024
     run = model_step(3, W.MODEL_360M, B, "newton", variant=capi.NDB_Z | capi.SYM_COUPLING)
-    picks, ef, ex, eu = sampled_parity(3, *run, B, "newton", capi.NDB_Z, 24, 10)
+    picks, ef, ex, eu, _ = sampled_parity(3, *run, B, "newton", capi.NDB_Z, 24, 10, count=2)
     report("config3_sym_coupling", blocks=picks, factor_err=ef, root_err=ex, U_err=eu)
     assert ef <= 1e-5 and ex <= TOL_F32 and eu <= TOL_F32
 
@@ -312,7 +321,7 @@ def test_config3_sampled_coupled_newton_fp16():
     """The pages' fastest configuration (coupled Newton in FP16) on the 360M-shaped step."""
     B = 1024
     run = model_step(3, W.MODEL_360M, B, "newton", variant=capi.CN_F16)
-    picks, ef, ex, eu = sampled_parity(3, *run, B, "newton", capi.CN, 24, 10)
+    picks, ef, ex, eu, _ = sampled_parity(3, *run, B, "newton", capi.CN, 24, 10, count=2)
     report("config3_cn_fp16", blocks=picks, factor_err=ef, root_err=ex, U_err=eu)
     assert ef <= 1e-5 and ex <= TOL_BF16 and eu <= TOL_BF16
 
@@ -321,8 +330,9 @@ def test_config3_sampled_coupled_newton_fp16():
 def test_config5_sampled_bf16_chebyshev():
     B = 2048
     run = model_step(5, W.MODEL_1_3B, B, "cheby", prec=capi.BF16_IN, degree=24)
-    picks, ef, ex, eu = sampled_parity(5, *run, B, "cheby", capi.NDB, 24, 10)
-    report("config5", blocks=picks, factor_err=ef, root_err=ex, U_err=eu)
+    picks, ef, ex, eu, (px, pu) = sampled_parity(5, *run, B, "cheby", capi.NDB, 24, 10)
+    report("config5", blocks=picks, factor_err=ef, root_err=ex, U_err=eu,
+           root_err_median=float(np.median(px)), U_err_median=float(np.median(pu)))
     assert ef <= TOL_BF16 and ex <= TOL_BF16 and eu <= TOL_BF16
 
 
