@@ -271,6 +271,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for the HBM byte counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured as HIP graphs (kernel figures from one eager step)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -415,33 +417,58 @@ def main(argv=None):
         graft_ms = g0.elapsed_time(g1)
         del params, moms, vels, gtabs
 
-    # Timing hook on every hooked kernel family during the timed steps.
-    cap = 64 * args.steps + 64
-    kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]
-    for e in kev:
-        e.record(stream)  # materialise the underlying HIP events
-    torch.cuda.synchronize()
-    handles = (ctypes.c_void_p * (2 * cap))(*[e.cuda_event for e in kev])
-    fams = (ctypes.c_int32 * cap)()
-    capi.check(capi.shampoo_timing_hook(capi.TIME_ALL, ctypes.addressof(handles), ctypes.addressof(fams), cap),
-               "timing hook")
+    # Timing hook on every hooked kernel family during eager steps.
+    def run_hooked(nsteps):
+        cap = 64 * nsteps + 64
+        kev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * cap)]
+        for e in kev:
+            e.record(stream)  # materialise the underlying HIP events
+        torch.cuda.synchronize()
+        handles = (ctypes.c_void_p * (2 * cap))(*[e.cuda_event for e in kev])
+        fams = (ctypes.c_int32 * cap)()
+        capi.check(capi.shampoo_timing_hook(capi.TIME_ALL, ctypes.addressof(handles), ctypes.addressof(fams), cap),
+                   "timing hook")
+        if kind != "factors":
+            state.t = 0  # the steps start with a root refresh
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(nsteps):
+            step(t)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        recorded = capi.shampoo_timing_count()
+        capi.shampoo_timing_hook(capi.TIME_OFF, None, None, 0)
+        if recorded >= cap:
+            print("bench.py: timing hook capacity reached; kernel figures cover the first launches only",
+                  file=sys.stderr)
+        per = {}
+        for i in range(recorded):
+            per.setdefault(int(fams[i]), []).append(kev[2 * i].elapsed_time(kev[2 * i + 1]))
+        return per, t1 - t0
 
-    if kind != "factors":
-        state.t = 0  # the timed steps start with a root refresh
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(args.steps):
-        step(t)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    recorded = capi.shampoo_timing_count()
-    capi.shampoo_timing_hook(capi.TIME_OFF, None, None, 0)
-    if recorded >= cap:
-        print("bench.py: timing hook capacity reached; kernel figures cover the first launches only",
-              file=sys.stderr)
-    per_fam = {}
-    for i in range(recorded):
-        per_fam.setdefault(int(fams[i]), []).append(kev[2 * i].elapsed_time(kev[2 * i + 1]))
+    if args.graph:
+        if kind == "factors":
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                do_scale()
+                do_root()
+            replays = [g.replay]
+        else:
+            replays = [state.capture(gt, ut).replay for gt, ut in tables]
+        hooked_steps = 1
+        per_fam, _ = run_hooked(hooked_steps)  # kernel figures from one eager step
+        if kind != "factors":
+            state.t = 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(args.steps):
+            replays[t % len(replays)]()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    else:
+        hooked_steps = args.steps
+        per_fam, elapsed = run_hooked(hooked_steps)
 
     traffic_rec = {}
     if os.path.exists(TRAFFIC_FILE):
@@ -467,7 +494,6 @@ def main(argv=None):
                         "traffic": traffic, "flops_per_launch": flops, "bytes_per_launch": nbytes,
                         "tflops": round(tflops, 2), "mfma_frac": round(tflops / peak_flops, 4),
                         "gbs": round(gbs, 1)})
-    elapsed = t1 - t0
     ms_step = 1e3 * elapsed / args.steps
     value = nf * refreshes / elapsed
     status = status_of().cpu()
@@ -478,7 +504,7 @@ def main(argv=None):
                     "frac": top["frac"], "traffic": top["traffic"], "kernel": top["kernel"],
                     "launches_timed": top["launches_timed"], "avg_launch_ms": top["avg_launch_ms"],
                     "flops_per_launch": top["flops_per_launch"], "bytes_per_launch": top["bytes_per_launch"],
-                    "share_of_step": round(top["total_ms"] / (1e3 * elapsed), 4)}
+                    "share_of_step": round(top["total_ms"] / hooked_steps / ms_step, 4)}
     half = wl["prec"] == capi.BF16_IN or (cfg.solver == "newton" and (cfg.variant & 0xff) == capi.CN_F16)
     out = {
         "metric": METRIC,
@@ -495,7 +521,8 @@ def main(argv=None):
         "data": ("synthetic N(0, 0.02^2) gradients of the workload's weight shapes, seeded" if kind != "factors"
                  else "synthetic SPD factors of the workload's recipe, seeded"),
         "config": dict({"workload": wl["name"], "B": B, "blocks": n, "factors": nf},
-                       **({"update_every": every} if every > 1 else {})),
+                       **({"update_every": every} if every > 1 else {}),
+                       **({"hip_graph": True} if args.graph else {})),
         "roofline": roofline,
         "kernels": kernels,
         "stages_ms": {k: round(v, 3) for k, v in stages.items()},

@@ -284,12 +284,48 @@ class ShampooBlocks:
         return self.t % self.cfg.update_every == 0
 
     def step(self, g_table, u_table, stream=None):
+        self._enqueue(g_table, u_table, self.refresh_due, stream)
+        self.t += 1
+
+    def _enqueue(self, g_table, u_table, refresh, stream=None):
+        """Enqueue one step's launches (no host-side state changes)."""
         c = self.cfg
         accumulate(g_table, self.factors, c.beta, 1.0 - c.beta, c.prec, self.ws["acc"], stream)
-        if self.refresh_due:
+        if refresh:
             self.update_roots(stream)
         precondition(self.roots, g_table, u_table, c.prec, self.ws["pre"], stream)
-        self.t += 1
+
+    def reserve(self):
+        """Allocate every workspace a step needs, so that later steps allocate
+        nothing (required before capture)."""
+        c, n, B = self.cfg, self.nblocks, self.cfg.B
+        nf = 2 * n
+        self.ws["acc"].get(capi.shampoo_workspace_bytes(capi.OP_ACCUMULATE, n, B, 0, c.prec))
+        self.ws["scale"].get(capi.shampoo_workspace_bytes(capi.OP_SCALE, nf, B, 0, F32))
+        if c.solver == "newton":
+            self.ws["root"].get(capi.shampoo_workspace_bytes(capi.OP_NEWTON, nf, B, c.variant, F32))
+        else:
+            self.ws["root"].get(capi.shampoo_workspace_bytes(capi.OP_CHEBY, nf, B, c.degree, c.prec))
+        self.ws["pre"].get(capi.shampoo_workspace_bytes(capi.OP_PRECONDITION, n, B, 0, c.prec))
+
+    def capture(self, g_table, u_table):
+        """Capture one step over these descriptor tables as HIP graphs (one with
+        a root refresh and, for update_every > 1, one with cached roots) and
+        return a StepGraph whose replay() runs the next step.  New gradients are
+        copied into the tensors the tables point to before each replay."""
+        if self.cfg.scale_mode == capi.SCALE_POWER and self.v0 is None:
+            raise ValueError("set the start vectors before capturing")
+        self.reserve()
+        torch.cuda.synchronize()
+        graphs = {}
+        for refresh in ((True,) if self.cfg.update_every == 1 else (True, False)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self._enqueue(g_table, u_table, refresh)
+            graphs[refresh] = g
+        torch.cuda.synchronize()
+        return StepGraph(self, graphs, (g_table, u_table))
+
 
     def update_roots(self, stream=None):
         c = self.cfg
@@ -301,3 +337,18 @@ class ShampooBlocks:
         else:
             invroot_cheby(self.factors, self.scale, c.p, c.degree, c.interval_eps, c.prec, self.roots,
                           self.status, self.ws["root"], stream)
+
+
+class StepGraph:
+    """Captured optimizer steps of a ShampooBlocks: replay() enqueues the next
+    step (refresh or cached roots, as the state's step count says) as one graph
+    launch on the current stream and advances the step count."""
+
+    def __init__(self, state, graphs, tables):
+        self.state = state
+        self.graphs = graphs
+        self._tables = tables  # keep the descriptor tables alive
+
+    def replay(self):
+        self.graphs[self.state.refresh_due].replay()
+        self.state.t += 1
