@@ -82,12 +82,18 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return t;
 }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even: gfx950's V_CVT_PK_BF16_F32 (NaN stays
+// NaN), two values per instruction when packed.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+// Two bf16 values (a in the low half) in one dword.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // fp32 -> fp16 bits, round to nearest even (hardware conversion).
@@ -102,21 +108,31 @@ __device__ __forceinline__ uint16_t to_h16(float x, int fmt) {
   return fmt == H16_F16 ? f32_to_f16_bits(x) : f32_to_bf16_bits(x);
 }
 
+// Two 16-bit values of format fmt (a in the low half) in one dword, each
+// rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_h16x2(float a, float b, int fmt) {
+  if (fmt == H16_F16) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  }
+  return pack_bf16x2(a, b);
+}
+
 // Four consecutive 16-bit copies of o at p (p 8-byte aligned).
 __device__ __forceinline__ void stg4_h16(uint16_t* p, const floatx4& o, int fmt) {
   u32x2 w;
-  w.x = (uint32_t)to_h16(o[0], fmt) | ((uint32_t)to_h16(o[1], fmt) << 16);
-  w.y = (uint32_t)to_h16(o[2], fmt) | ((uint32_t)to_h16(o[3], fmt) << 16);
+  w.x = pack_h16x2(o[0], o[1], fmt);
+  w.y = pack_h16x2(o[2], o[3], fmt);
   stg(reinterpret_cast<u32x2*>(p), w);
 }
 
 // Eight consecutive 16-bit copies of lo, hi at p (p 16-byte aligned).
 __device__ __forceinline__ void stg8_h16(uint16_t* p, const floatx4& lo, const floatx4& hi, int fmt) {
   u32x4 w;
-  w.x = (uint32_t)to_h16(lo[0], fmt) | ((uint32_t)to_h16(lo[1], fmt) << 16);
-  w.y = (uint32_t)to_h16(lo[2], fmt) | ((uint32_t)to_h16(lo[3], fmt) << 16);
-  w.z = (uint32_t)to_h16(hi[0], fmt) | ((uint32_t)to_h16(hi[1], fmt) << 16);
-  w.w = (uint32_t)to_h16(hi[2], fmt) | ((uint32_t)to_h16(hi[3], fmt) << 16);
+  w.x = pack_h16x2(lo[0], lo[1], fmt);
+  w.y = pack_h16x2(lo[2], lo[3], fmt);
+  w.z = pack_h16x2(hi[0], hi[1], fmt);
+  w.w = pack_h16x2(hi[2], hi[3], fmt);
   stg(reinterpret_cast<u32x4*>(p), w);
 }
 

@@ -313,14 +313,14 @@ __global__ void __launch_bounds__(256) bf16_cast_kernel(const CastArgs P) {
     const int lr = cr + 16 * i;
     if (P.out) {
       u32x2 w;
-      w.x = (uint32_t)f32_to_bf16_bits(t[lr][cc]) | ((uint32_t)f32_to_bf16_bits(t[lr][cc + 1]) << 16);
-      w.y = (uint32_t)f32_to_bf16_bits(t[lr][cc + 2]) | ((uint32_t)f32_to_bf16_bits(t[lr][cc + 3]) << 16);
+      w.x = pack_bf16x2(t[lr][cc], t[lr][cc + 1]);
+      w.y = pack_bf16x2(t[lr][cc + 2], t[lr][cc + 3]);
       stg(reinterpret_cast<u32x2*>(P.out + base + (int64_t)(r0 + lr) * P.B + c0 + cc), w);
     }
     if (P.out_t) {
       u32x2 w;
-      w.x = (uint32_t)f32_to_bf16_bits(t[cc][lr]) | ((uint32_t)f32_to_bf16_bits(t[cc + 1][lr]) << 16);
-      w.y = (uint32_t)f32_to_bf16_bits(t[cc + 2][lr]) | ((uint32_t)f32_to_bf16_bits(t[cc + 3][lr]) << 16);
+      w.x = pack_bf16x2(t[cc][lr], t[cc + 1][lr]);
+      w.y = pack_bf16x2(t[cc + 2][lr], t[cc + 3][lr]);
       stg(reinterpret_cast<u32x2*>(P.out_t + base + (int64_t)(c0 + lr) * P.B + r0 + cc), w);
     }
   }

@@ -663,10 +663,10 @@ __global__ void __launch_bounds__(256) ew_kernel(const EwArgs P) {
     }
     if (MODE == EW_CN16_START) {
       u32x2 w0, w1;
-      w0.x = (uint32_t)to_h16(o0[0], P.fmt16) | ((uint32_t)to_h16(o0[1], P.fmt16) << 16);
-      w0.y = (uint32_t)to_h16(o0[2], P.fmt16) | ((uint32_t)to_h16(o0[3], P.fmt16) << 16);
-      w1.x = (uint32_t)to_h16(o1[0], P.fmt16) | ((uint32_t)to_h16(o1[1], P.fmt16) << 16);
-      w1.y = (uint32_t)to_h16(o1[2], P.fmt16) | ((uint32_t)to_h16(o1[3], P.fmt16) << 16);
+      w0.x = pack_h16x2(o0[0], o0[1], P.fmt16);
+      w0.y = pack_h16x2(o0[2], o0[3], P.fmt16);
+      w1.x = pack_h16x2(o1[0], o1[1], P.fmt16);
+      w1.y = pack_h16x2(o1[2], o1[3], P.fmt16);
       stg(reinterpret_cast<u32x2*>(P.h0 + off + 4 * i), w0);
       stg(reinterpret_cast<u32x2*>(P.h1 + off + 4 * i), w1);
     }
