@@ -78,6 +78,10 @@ int ew_chunks(int B) {
 // largest of these whose grid still gives every compute unit a workgroup,
 // and the 64 x 64 tiles when none does (a small batch is bound by how many
 // compute units it occupies, not by the per-tile efficiency of larger tiles).
+// The large tiles run one workgroup per compute unit, so their grid is also
+// taken only when it fills whole rounds of the GPU or at least four rounds
+// (a grid of 1.5 rounds leaves half the GPU idle in its second round; the
+// 128 x 128 kernel runs several workgroups per unit and balances there).
 constexpr int64_t kComputeUnits = 256;
 
 template <class Epi>
@@ -87,8 +91,12 @@ int f32_tile_edge(int B, bool sym, bool dense, int64_t items) {
     return items * (sym ? t * (t + 1) / 2 : t * t);
   };
   const bool fits = sym ? Epi::kBigSym : Epi::kBigFull;
-  if (dense && fits && B % kBigTile == 0 && grid(kBigTile) >= kComputeUnits) return kBigTile;
-  if (B % 128 == 0 && grid(128) >= kComputeUnits) return 128;
+  const bool mid = B % 128 == 0 && grid(128) >= kComputeUnits;
+  if (dense && fits && B % kBigTile == 0 && grid(kBigTile) >= kComputeUnits) {
+    const int64_t g = grid(kBigTile);
+    if (g % kComputeUnits == 0 || g >= 4 * kComputeUnits || !mid) return kBigTile;
+  }
+  if (mid) return 128;
   return 64;
 }
 

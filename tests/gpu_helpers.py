@@ -75,12 +75,13 @@ def oracle_root(F, sc, method, iters=10, p=4, variant=capi.NDB, degree=24, delta
     return O.invroot(F, sc, "cheby", p=p, degree=degree, delta=delta)
 
 
-def fill_factor(B, per_factor_tiles, base, cus=256):
+def fill_factor(B, per_factor_tiles, base, cus=256, rounds=4):
     """How many copies of `base` checked factors a stack needs so that a launch
-    over it has at least `cus` workgroups of `per_factor_tiles` tiles per
-    factor: below that, the library picks smaller tiles to fill the GPU, so
-    tests meant for the large-tile kernels replicate their factors."""
-    need = -(-cus // per_factor_tiles)
+    over it has at least `rounds` x `cus` workgroups of `per_factor_tiles`
+    tiles per factor.  The library takes the 256 x 256 tiles only when their
+    grid fills the GPU in whole rounds or in at least four rounds (else smaller
+    tiles), so tests meant for the large-tile kernels replicate their factors."""
+    need = -(-(rounds * cus) // per_factor_tiles)
     return -(-need // base)
 
 
