@@ -285,7 +285,12 @@ __device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, float
 // KPRE bounds how many groups' epilogue inputs are loaded ahead (registers).
 //
 // SP > 0: both halves go through `stage`, this wave's 32 x (32 SP + 4) floats
-// of LDS.  Each group is first written there at its transposed place; once
+// of LDS; entry (x, y) sits at x (32 SP + 4) + (y ^ 8 SP) for x >= 16, else at
+// x (32 SP + 4) + y: unswizzled, staged rows x and x + 16 start on the same
+// bank, and the column-wise reads of the upper half below went two lanes to a
+// bank.  For SP = 1 each 16-lane pass of the row-wise reads takes two rows 8
+// apart, whose 32 floats fill complementary halves of the 64 banks (rows 1
+// apart overlap on 4).  Each group is first written there at its transposed place; once
 // the SP vertically adjacent blocks of one column are in, the wave reads them
 // back along the mirrored rows, each store instruction covering 32 SP
 // consecutive columns of 64 / (8 SP) rows (whole 128-byte lines, where a
@@ -300,7 +305,11 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
                                                     int wn, int lane, bool diag, int mask, float* stage = nullptr) {
   static_assert(SP == 0 || (TM % SP == 0 && SP <= 2), "staged blocks per column");
   constexpr int LDT = 32 * SP + 4;  // staged row pitch in floats: the group writes of 16 lanes hit 64 banks
+  constexpr int SWZ = 8 * SP;       // column swizzle of staged rows 16..31
   const int h = lane >> 5, cl = lane & 31;
+  // staged-row base of this lane's group writes (row cl), for columns with the swizzle bit clear or set
+  const int sw_w = (cl & 16) ? SWZ : 0;
+  const int st_plus = cl * LDT + 4 * h + sw_w, st_minus = cl * LDT + 4 * h - sw_w;
   // group G -> block (i, j), accumulators 4 q .. 4 q + 3
   auto gi_ = [](int g) { return SP ? (g / 4) % TM : g / (TN * 4); };
   auto gj_ = [](int g) { return SP ? g / (TM * 4) : (g / 4) % TN; };
@@ -327,7 +336,8 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
     if constexpr (SP > 0) {
       constexpr int g = decltype(G)::value;
       constexpr int i = gi_(g), q = g % 4;
-      *reinterpret_cast<floatx4*>(stage + cl * LDT + 32 * (i % SP) + 8 * q + 4 * h) = o;
+      constexpr int y = 32 * (i % SP) + 8 * q;  // y ^ sw = y + sw or y - sw by the bit y holds
+      *reinterpret_cast<floatx4*>(stage + ((y & SWZ) ? st_minus : st_plus) + y) = o;
     }
   };
   // After the last group of the SP blocks of one column, computed or not: the
@@ -343,14 +353,17 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
         __builtin_amdgcn_wave_barrier();
         constexpr int LPR = 8 * SP;    // lanes per staged row
         constexpr int RPI = 64 / LPR;  // rows per instruction
-        const int rr = lane / LPR, cc = 4 * (lane % LPR);
+        const int rr = lane / LPR, cc = 4 * (lane % LPR), cc_sw = cc ^ SWZ;
+        // row of instruction t: RPI t + rr, or for SP = 1 rows 8 apart in each pass of 16 lanes
+        const int rrow = SP == 1 ? 8 * (rr & 1) + (rr >> 1) : rr;
         const int c0 = n0 + wn + 32 * j, r0 = m0 + wm + 32 * i0;
         // on a diagonal tile: whether this lane's source block was computed by this wave
         const bool src = !decltype(DG)::value || ((mask >> ((i0 + cc / 32) * TN + j)) & 1);
 #pragma unroll
         for (int t = 0; t < 32 / RPI; ++t) {
-          const int row = RPI * t + rr;
-          const floatx4 v = *reinterpret_cast<const floatx4*>(stage + row * LDT + cc);
+          const int tb = SP == 1 ? 4 * (t & 1) + 16 * (t >> 1) : RPI * t;  // >= 16 exactly for swizzled rows
+          const int row = tb + rrow;
+          const floatx4 v = *reinterpret_cast<const floatx4*>(stage + row * LDT + (tb >= 16 ? cc_sw : cc));
           if constexpr (!decltype(DG)::value) {
             tile.write4t(c0 + row, r0 + cc, v);
           } else if (src) {
@@ -369,15 +382,16 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
         // by group; 8 measured slower for the fp32 kernel).
         constexpr int CU = SP == 2 ? 8 : 4, LPU = 32 / CU, RPU = 64 / LPU;
         const int ru = lane / LPU, cu = CU * (lane % LPU);
+        const int sw_u = (cu & 16) ? SWZ : 0;  // the staged rows cu .. cu + CU - 1 share bit 4
         constexpr int NU = 32 * SP / RPU;  // iterations
         auto upper = [&](int t) __attribute__((always_inline)) {
-          const int rl = RPU * t + ru;
+          const int rl = RPU * t + ru, rs = rl ^ sw_u;
           floatx4 lo, hi;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) lo[e] = stage[(cu + e) * LDT + rl];
+          for (int e = 0; e < 4; ++e) lo[e] = stage[(cu + e) * LDT + rs];
           if constexpr (CU == 8) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hi[e] = stage[(cu + 4 + e) * LDT + rl];
+            for (int e = 0; e < 4; ++e) hi[e] = stage[(cu + 4 + e) * LDT + rs];
           }
           const int r = r0 + rl, c = c0 + cu;
           const bool whole = !decltype(DG)::value || r <= c;
