@@ -378,7 +378,7 @@ __global__ void __launch_bounds__(256, 2) pi_step_dma_kernel(const PiArgs P) {
   const int j = lane & 31;
   const float sj = s_col[j];
   const float eps = P.sc[f].eps;
-    const float rinv = pow2f(-range_exp(P.sc[f].trace, P.B));
+  const float rinv = pow2f(-range_exp(P.sc[f].trace, P.B));
   float nsum = 0.f, rsum = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -509,7 +509,7 @@ __global__ void __launch_bounds__(512, 2) pi_step_col_kernel(const PiArgs P) {
   const int j = lane & 31;
   const float sj = s_col[j];
   const float eps = P.sc[f].eps;
-    const float rinv = pow2f(-range_exp(P.sc[f].trace, P.B));
+  const float rinv = pow2f(-range_exp(P.sc[f].trace, P.B));
   float nsum = 0.f, rsum = 0.f;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {

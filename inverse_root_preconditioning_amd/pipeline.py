@@ -326,7 +326,6 @@ class ShampooBlocks:
         torch.cuda.synchronize()
         return StepGraph(self, graphs, (g_table, u_table))
 
-
     def update_roots(self, stream=None):
         c = self.cfg
         scale_power(self.factors, c.eps_rel, c.scale_mode, self.v0, c.pi_steps, c.safety, self.scale,
