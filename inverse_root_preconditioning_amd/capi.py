@@ -112,6 +112,11 @@ def load(path=None):
     if not os.path.exists(p):
         raise RuntimeError(f"HIP library not built: {p} is missing "
                            "(run `python -m inverse_root_preconditioning_amd.build`)")
+    # PyTorch ships its own HIP runtime.  It is loaded first so that this
+    # library binds to that copy: with a second runtime in the process, the
+    # launches here would not see the streams and memory the caller got from
+    # PyTorch and would fail.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)

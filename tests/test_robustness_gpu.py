@@ -149,3 +149,32 @@ def test_checkpoint_resume_is_bitwise(update_every):
     for (ua, fa, xa), (ub, fb, xb) in zip(full[3:], tail):
         assert np.array_equal(ua, ub) and np.array_equal(fa, fb) and np.array_equal(xa, xb)
     report("checkpoint_resume", update_every=update_every, ok=True)
+
+
+_LOAD_FIRST = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+from inverse_root_preconditioning_amd import capi
+capi.load()                      # the library before any explicit torch import
+import torch
+from inverse_root_preconditioning_amd import pipeline as PL
+g = torch.randn((2, 64, 64), device="cuda")
+F = torch.zeros((4, 64, 64), device="cuda")
+PL.accumulate(PL.BlockTable.from_stack(g), F, 0.0, 1.0)
+torch.cuda.synchronize()
+ref = torch.cat([g @ g.transpose(1, 2), g.transpose(1, 2) @ g])
+err = ((F - ref).norm() / ref.norm()).item()
+print("ok" if err < 1e-5 else f"err {err}")
+"""
+
+
+def test_library_loaded_before_torch():
+    """Loading the library before PyTorch must still bind it to PyTorch's HIP
+    runtime (a second runtime in the process fails every launch)."""
+    import subprocess
+    import sys
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", _LOAD_FIRST, root], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "ok", out.stdout
