@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(H16Shape<CFG>::NT, H16Shape<CFG>::MINW)
   float part = 0.f;
   if constexpr (CFG == H16_T256) {
     constexpr int PH = (sizeof(lds) >= sizeof(float) * BM * (BN + 1)) ? 1 : 2;
-    static_assert(sizeof(lds) >= sizeof(float) * (BM / PH) * (BN + 1), "LDS too small for the staging");
+    static_assert(sizeof(lds) >= sizeof(float) * (BM / PH) * (BN + 4), "LDS too small for the staging");
     constexpr bool kDirect = [] {
       if constexpr (Epi::kSym) return Epi::kDirect && !Epi::kReduce && SYM;
       return false;
@@ -417,7 +417,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
   constexpr int PH = 4;                                  // phases of the symmetric epilogue's transpose
   constexpr int kFloats = 2 * kStage / 2;                // the stage buffers, counted in floats
   static_assert(LA * NT == BM * CPR && BN == BM, "chunking");
-  static_assert((BM / PH) * (BN + 1) + NT / kWave <= kFloats, "transpose and reduction fit the buffers");
+  static_assert((BM / PH) * (BN + 4) + NT / kWave <= kFloats, "staging and reduction fit the buffers");
   // One LDS object only (see gemm_f32_big_kernel).
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
   float* const red = reinterpret_cast<float*>(lds) + kFloats - NT / kWave;
@@ -577,8 +577,8 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
 
   if constexpr (WAVES == 8 && !kDirectSym) {
     typename Epi::Tile tile(*(job == 0 ? &P.e[0] : &P.e[1]), item, P.B);
-    const float part = staged_epilogue<TM, TN, BM, BN, NT, PH, Epi>(tile, acc, reinterpret_cast<float*>(lds), m0,
-                                                                    n0, wm, wn, lane, SYM, tm == tn);
+    const float part = staged_epilogue<TM, TN, BM, BN, NT, PH, Epi, !SYM>(tile, acc, reinterpret_cast<float*>(lds),
+                                                                          m0, n0, wm, wn, lane, SYM, tm == tn);
     if constexpr (Epi::kReduce) {
       const float tot = block_sum<NT>(part, red);
       if (threadIdx.x == 0) {
