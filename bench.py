@@ -50,6 +50,20 @@ F32_SOURCES = ["common.h", "gemm_f32.h"]
 H16_SOURCES = ["common.h", "gemm_f32.h", "gemm_bf16.h"]
 
 
+ALL_SOURCES = ["common.h", "gemm_f32.h", "gemm_bf16.h", "kernels_misc.h", "shampoo.hip"]
+
+
+def env_info():
+    """Software and device the line was measured with (the box has no git checkout, so the library
+    sources are identified by their digest)."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    return {"hip": torch.version.hip, "torch": torch.__version__, "gpu": props.name,
+            "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+            "library_sources_digest": source_digest(ALL_SOURCES),
+            "seeds": "numpy PCG64(SeedSequence([config, tag, index...])), drawn in float64, rounded once to fp32"}
+
+
 def source_digest(files):
     h = hashlib.sha256()
     for s in files:
@@ -531,6 +545,7 @@ def main(argv=None):
     }
     if graft_ms is not None:
         out["graft_update_ms"] = round(graft_ms, 3)
+    out["env"] = env_info()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, cpu_inputs, args.cpu_budget)
     print(json.dumps(out), flush=True)
