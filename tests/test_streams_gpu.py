@@ -1,8 +1,10 @@
 """Streams: calls on different streams with distinct workspaces may run at
-the same time.  Two factor sets go through scale, Newton-DB and the bf16
-Chebyshev root on two side streams at once (each with its own workspace),
-and every result must equal, bit for bit, the same calls run one after the
-other on the default stream (fixed reduction orders, no shared state)."""
+the same time.  Two factor sets go through scale, Newton-DB, the bf16
+Chebyshev root and fp16 coupled Newton on two side streams at once (each
+with its own workspace), and two whole optimizer states take two steps each
+on two side streams at once; every result must equal, bit for bit, the same
+calls run one after the other on the default stream (fixed reduction orders,
+no shared state)."""
 import numpy as np
 import pytest
 import torch
@@ -32,7 +34,9 @@ def _chain(F, V, ws, stream):
     PL.invroot_newton(F, sc, 4, capi.NDB_Z, 6, X, st, R, ws=ws, stream=stream)
     Xc = torch.empty_like(F)
     PL.invroot_cheby(F, sc, 4, 12, 1e-12, capi.BF16_IN, Xc, st, ws=ws, stream=stream)
-    return sc, st, X, R, Xc
+    Xh = torch.empty_like(F)
+    PL.invroot_newton(F, sc, 4, capi.CN_F16, 6, Xh, st, ws=ws, stream=stream)
+    return sc, st, X, R, Xc, Xh
 
 
 def test_concurrent_streams_match_sequential():
@@ -53,6 +57,43 @@ def test_concurrent_streams_match_sequential():
     for (F, V), s, ws in zip(sets, streams, wss):
         with torch.cuda.stream(s):
             outs.append(_chain(F, V, ws, s))
+    torch.cuda.synchronize()
+    for r, o in zip(ref, outs):
+        for a, b in zip(r, o):
+            assert np.array_equal(a, host(b))
+
+
+def _steps(cfg, grads, v0, stream):
+    """Two optimizer steps (accumulate, scale, roots, precondition) of one state."""
+    n = grads[0].shape[0]
+    state = PL.ShampooBlocks(cfg, n)
+    state.set_start_vectors(v0)
+    outs = []
+    for g in grads:
+        u = torch.zeros_like(g)
+        state.step(PL.BlockTable.from_stack(g), PL.BlockTable.from_stack(u), stream)
+        outs.append(u)
+    return [state.factors, state.roots, state.scale, state.status] + outs
+
+
+def test_concurrent_optimizer_steps_match_sequential():
+    B, n = 256, 24
+    cfgs = [PL.StepConfig(B, variant=capi.NDB_Z, iters=8),
+            PL.StepConfig(B, solver="cheby", degree=16, prec=capi.BF16_IN)]
+    runs = []
+    for k, cfg in enumerate(cfgs):
+        grads = [dev(np.stack([W.gaussian((40 + k, 1, t, i), (B, B)) for i in range(n)])) for t in range(2)]
+        v0 = dev(W.start_vectors(50 + k, 2 * n, B))
+        runs.append((cfg, grads, v0))
+    torch.cuda.synchronize()
+    ref = [[host(t) for t in _steps(cfg, grads, v0, None)] for cfg, grads, v0 in runs]
+
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+    torch.cuda.synchronize()
+    outs = []
+    for (cfg, grads, v0), s in zip(runs, streams):
+        with torch.cuda.stream(s):
+            outs.append(_steps(cfg, grads, v0, s))
     torch.cuda.synchronize()
     for r, o in zip(ref, outs):
         for a, b in zip(r, o):
