@@ -323,6 +323,20 @@ __device__ __forceinline__ float staged_epilogue(typename Epi::Tile& tile, float
 // only entries of computed blocks on (upper) or strictly below (mirrored) the
 // diagonal go out.
 // Groups are then taken column of blocks by column of blocks (j-major).
+// Mirrored entries of an off-diagonal tile: write4t_mirror where the tile has
+// one (an output kept partly on and above the diagonal only), else write4t.
+template <class T, class = void>
+struct has_write4t_mirror : std::false_type {};
+template <class T>
+struct has_write4t_mirror<T, std::void_t<decltype(&T::write4t_mirror)>> : std::true_type {};
+template <class Tile>
+__device__ __forceinline__ void write4t_offdiag(Tile& t, int c, int r, const floatx4& o) {
+  if constexpr (has_write4t_mirror<Tile>::value)
+    t.write4t_mirror(c, r, o);
+  else
+    t.write4t(c, r, o);
+}
+
 template <int TM, int TN, int KPRE, int SP = 0, class Tile>
 __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[TM][TN], int m0, int n0, int wm,
                                                     int wn, int lane, bool diag, int mask, float* stage = nullptr) {
@@ -388,7 +402,7 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
           const int row = tb + rrow;
           const floatx4 v = *reinterpret_cast<const floatx4*>(stage + row * LDT + (tb >= 16 ? cc_sw : cc));
           if constexpr (!decltype(DG)::value) {
-            tile.write4t(c0 + row, r0 + cc, v);
+            write4t_offdiag(tile, c0 + row, r0 + cc, v);
           } else if (src) {
             if (r0 + cc + 3 < c0 + row) {
               tile.write4t(c0 + row, r0 + cc, v);
@@ -1226,6 +1240,7 @@ struct EpiCnM {
 //   X = mult (cj I + 2 acc - b1 - b2), I if degenerate   (final == 1, cj = c_0)
 // An optional 16-bit copy of b is written for the next half-width product.
 struct EpiClenshaw {
+  static constexpr bool kH16AUpper = true;  // may keep its 16-bit copy on and above the diagonal only
   static constexpr bool kReduce = false;
   static constexpr bool kSym = true;
   static constexpr bool kDirect = true;
@@ -1247,6 +1262,7 @@ struct EpiClenshaw {
     const shampoo_scale* scale;
     const int32_t* status;
     float pexp;
+    int upper16;         // the 16-bit copy only in tiles on and above the diagonal (mirrored half not written)
   };
   struct Tile {
     static constexpr int kPrefetch = 4;  // groups whose b1, b2 are loaded per chunk
@@ -1259,9 +1275,10 @@ struct EpiClenshaw {
     const float* b1;
     const float* b2;
     float cj, mult, k1, k2, c2;
-    bool ident, is_final, b2_diag;
+    bool ident, is_final, b2_diag, upper16;
     int B;
     __device__ __forceinline__ Tile(const Job& j, int64_t item, int B_) : B(B_) {
+      upper16 = j.upper16 != 0;
       const int64_t off = item * (int64_t)B_ * B_;
       out = j.out + off;
       obf = j.out16 ? j.out16 + off : nullptr;
@@ -1320,6 +1337,13 @@ struct EpiClenshaw {
       const int64_t idx = (int64_t)c * B + r;
       stg(reinterpret_cast<floatx4*>(out + idx), o);
       if (obf) stg4_h16(obf + idx, o, fmt);
+    }
+    // the mirrored entries of an off-diagonal tile: the 16-bit copy there only
+    // when it is kept in full (upper16 clear); fp32 b is read back there
+    __device__ __forceinline__ void write4t_mirror(int c, int r, const floatx4& o) {
+      const int64_t idx = (int64_t)c * B + r;
+      stg(reinterpret_cast<floatx4*>(out + idx), o);
+      if (obf && !upper16) stg4_h16(obf + idx, o, fmt);
     }
     // When the next product takes its operand from the 16-bit copy, an
     // intermediate fp32 b is read back only at transposed positions (value4),

@@ -942,8 +942,12 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
     a.c1 = (float)c[degree - 1];
     SHP_TRY(run_ew<EW_CHEBY_START>(a, nf, st));
   }
+  // bf16 terms on the large-tile kernel keep their 16-bit copy only in the tiles
+  // on and above the diagonal; the next product reads the rest transposed
+  const bool up = bf && sym && (B % kBigTile) == 0;
   for (int j = degree - 2; j >= 0; --j) {
     EpiClenshaw::Job e;
+    e.upper16 = up ? 1 : 0;
     e.out = (j == 0) ? x : ws->b[i0];
     e.out16 = (bf && j > 0) ? ws->b16[s1 ^ 1] : nullptr;
     e.fmt16 = H16_BF16;
@@ -957,7 +961,7 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
     e.pexp = pexp;
     if (bf) {
       timing_before(SHAMPOO_TIME_CLENSHAW, st);
-      const int rc = bf16_gemm_nt_clenshaw(ws->b16[s1], ws->as_t16, e, nf, B, sym, st);
+      const int rc = bf16_gemm_nt_clenshaw(ws->b16[s1], ws->as_t16, e, nf, B, sym, up, st);
       timing_after(SHAMPOO_TIME_CLENSHAW, st);
       SHP_TRY(rc);
       s1 ^= 1;
