@@ -49,11 +49,14 @@ struct H16Launch {
   int tiles_n;
   int tiles_per_item;
   uint32_t total;      // njobs * nitems * tiles_per_item
-  // A is symmetric and stored only in its 256 x 256 tiles on and above the
-  // diagonal (gemm_h16_big_kernel, symmetric products): row panel I takes its
-  // k-blocks K < I from tile (K, I), transposed
-  int a_upper;
+  // Operands stored only in their 256 x 256 tiles on and above the diagonal
+  // (symmetric matrices; gemm_h16_big_kernel): bit 2 j (H16_UPPER_A) for A of
+  // job j, bit 2 j + 1 (H16_UPPER_B) for its Bt.  Row panel I of such an
+  // operand takes its k-blocks K < I from tile (K, I), transposed.
+  int upper;
 };
+
+enum { H16_UPPER_A = 1, H16_UPPER_B = 2 };
 
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -377,18 +380,19 @@ static inline int bf16_gather(const shampoo_block* d, int64_t n, int B, uint16_t
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int h16_swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// Transposed A stages (H16Launch::a_upper): 64 k-rows of 256 columns, the
+// Transposed operand stages (H16Launch::upper): 64 k-rows of 256 columns, the
 // 16-byte chunk index of row kr XOR-ed with h16_tswz(kr), so that the
 // column-wise fragment reads of 4 rows (ds_read_b64_tr_b16) fall on 4
 // different quarters of the 64 banks.
 __device__ __forceinline__ int h16_tswz(int kr) { return 4 * (kr & 3); }
 
-// Epilogues that can keep their 16-bit output only on and above the diagonal
-// (for a next product that reads it with H16Launch::a_upper).
+// Epilogues whose large-tile kernel is built with the transposed stages, so
+// that its operands may be kept on and above the diagonal only
+// (H16Launch::upper).
 template <class T, class = void>
-struct has_a_upper : std::false_type {};
+struct has_upper_operands : std::false_type {};
 template <class T>
-struct has_a_upper<T, std::void_t<decltype(T::kH16AUpper)>> : std::integral_constant<bool, T::kH16AUpper> {};
+struct has_upper_operands<T, std::void_t<decltype(T::kH16Upper)>> : std::integral_constant<bool, T::kH16Upper> {};
 
 // 8 waves of 64 x 128 on a 256 x 256 tile: wave w takes block row r (64
 // rows) and column half c (128 columns) from a fixed placement.  On a
@@ -471,31 +475,43 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
   }
   const int rr = lane & 31, h = lane >> 5;
 
+  constexpr bool kUpper = has_upper_operands<Epi>::value;
   const uint16_t* srcA[LA];
   const uint16_t* srcB[LA];
-  const uint16_t* srcAT[LA];
+  const uint16_t* srcAT[kUpper ? LA : 1];
+  const uint16_t* srcBT[kUpper ? LA : 1];
 #pragma unroll
   for (int it = 0; it < LA; ++it) {
     const int c = it * NT + tid, row = c / CPR, cs = (c % CPR) ^ h16_swz(c / CPR);
     srcA[it] = A + (int64_t)(m0 + row) * B + 8 * cs;
     srcB[it] = Bt + (int64_t)(n0 + row) * B + 8 * cs;
-    // transposed stage: row kr of the 64 k-rows, 16-byte chunk cc of its 256 columns (h16_tswz)
-    const int kr = c / (BM / 8), cc = c % (BM / 8);
-    srcAT[it] = A + (int64_t)kr * B + m0 + 8 * (cc ^ h16_tswz(kr));
+    if constexpr (kUpper) {
+      // transposed stage: row kr of the 64 k-rows, 16-byte chunk cc of its 256 columns (h16_tswz)
+      const int kr = c / (BM / 8), cc = c % (BM / 8);
+      srcAT[it] = A + (int64_t)kr * B + m0 + 8 * (cc ^ h16_tswz(kr));
+      srcBT[it] = Bt + (int64_t)kr * B + n0 + 8 * (cc ^ h16_tswz(kr));
+    }
   }
   const int nstages = B / BKS;
-  // stages whose A panel comes transposed from the upper tiles (k-blocks above row block tm)
-  const int ntrans = (SYM && has_a_upper<Epi>::value && P.a_upper) ? min(m0 / BKS, nstages) : 0;
+  // stages whose A (Bt) panel comes transposed from the upper tiles: the
+  // k-blocks left of the diagonal tile of row block tm (tn)
+  const int up = kUpper ? (P.upper >> (2 * job)) & 3 : 0;
+  const int ntA = (up & H16_UPPER_A) ? min(m0 / BKS, nstages) : 0;
+  const int ntB = (up & H16_UPPER_B) ? min(n0 / BKS, nstages) : 0;
   auto issue = [&](uint16_t* __restrict__ buf, int s) __attribute__((always_inline)) {
     const int k0 = min(s, nstages - 1) * BKS;
-    const bool trans = s < ntrans;
 #pragma unroll
     for (int it = 0; it < LA; ++it) {
-      const uint16_t* pa = trans ? srcAT[it] + (int64_t)k0 * B : srcA[it] + k0;
+      const uint16_t* pa = srcA[it] + k0;
+      const uint16_t* pb = srcB[it] + k0;
+      if constexpr (kUpper) {
+        if (s < ntA) pa = srcAT[it] + (int64_t)k0 * B;
+        if (s < ntB) pb = srcBT[it] + (int64_t)k0 * B;
+      }
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pa,
                                        (__attribute__((address_space(3))) void*)(buf + (it * NT + wave * 64) * 8),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(srcB[it] + k0),
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pb,
                                        (__attribute__((address_space(3))) void*)(buf + kA + (it * NT + wave * 64) * 8),
                                        16, 0, 0);
     }
@@ -516,15 +532,14 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
   __builtin_amdgcn_s_waitcnt(kWaitAll);
   __builtin_amdgcn_s_barrier();
 
-  constexpr bool kAUpper = SYM && has_a_upper<Epi>::value;
   auto mainloop = [&](auto M) __attribute__((always_inline)) {
     constexpr int kMask = decltype(M)::value;
     // One stage: the loads for stage s + 1 into `wr` (read at stage s - 1,
-    // free since that stage's barrier), then the MFMAs on `rd`.  TR: A was
-    // staged transposed ([k][m], h16_tswz).
-    auto step = [&](auto TRc, const uint16_t* __restrict__ rd, uint16_t* __restrict__ wr, int s)
+    // free since that stage's barrier), then the MFMAs on `rd`.  TA (TB): A
+    // (Bt) was staged transposed ([k][m], h16_tswz).
+    auto step = [&](auto TAc, auto TBc, const uint16_t* __restrict__ rd, uint16_t* __restrict__ wr, int s)
         __attribute__((always_inline)) {
-      constexpr bool TR = decltype(TRc)::value;
+      constexpr bool TA = decltype(TAc)::value, TB = decltype(TBc)::value;
       issue(wr, s + 1);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kMask != 0) {
@@ -543,28 +558,36 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
         auto frag = [&](const uint16_t* base, int row, int ks) __attribute__((always_inline)) {
           return *reinterpret_cast<const u32x4*>(base + (row * CPR + ((2 * ks + h) ^ h16_swz(row))) * 8);
         };
-        // A fragment of block row i from a transposed stage: in each group of 16
-        // lanes, lane 4 p + q addresses k-row 16 ks + 8 h + p (+ 4) at column
-        // wm + 32 i + 16 (group & 1) + 4 q, and ds_read_b64_tr_b16 hands lane t
-        // of the group column t of those at the 4 rows: 8 consecutive k of one
-        // row of A, as the MFMA takes them.
-        auto fragA = [&](const uint16_t* base, int i, int ks) __attribute__((always_inline)) {
-          if constexpr (TR) {
-            const int p = (lane >> 2) & 3, m = wm + 32 * i + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-            u32x4 r;
+        // The fragment of rows col .. col + 31 from a transposed stage: in each
+        // group of 16 lanes, lane 4 p + q addresses k-row 16 ks + 8 h + p (+ 4)
+        // at column col + 16 (group & 1) + 4 q, and ds_read_b64_tr_b16 hands
+        // lane t of the group column t of those at the 4 rows: 8 consecutive k
+        // of one row of the operand, as the MFMA takes them (A and Bt alike).
+        auto fragT = [&](const uint16_t* base, int col, int ks) __attribute__((always_inline)) {
+          const int p = (lane >> 2) & 3, m = col + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+          u32x4 r;
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              const int kr = 16 * ks + 8 * h + p + 4 * half;
-              const uint16_t* a = base + (kr * (BM / 8) + ((m >> 3) ^ h16_tswz(kr))) * 8 + (m & 7);
-              const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)a);
-              const u32x2 w = __builtin_bit_cast(u32x2, v);
-              r[2 * half] = w.x;
-              r[2 * half + 1] = w.y;
-            }
-            return r;
-          } else {
-            return frag(base, wm + 32 * i + rr, ks);
+          for (int half = 0; half < 2; ++half) {
+            const int kr = 16 * ks + 8 * h + p + 4 * half;
+            const uint16_t* a = base + (kr * (BM / 8) + ((m >> 3) ^ h16_tswz(kr))) * 8 + (m & 7);
+            const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)a);
+            const u32x2 w = __builtin_bit_cast(u32x2, v);
+            r[2 * half] = w.x;
+            r[2 * half + 1] = w.y;
           }
+          return r;
+        };
+        auto fragA = [&](const uint16_t* base, int i, int ks) __attribute__((always_inline)) {
+          if constexpr (TA)
+            return fragT(base, wm + 32 * i, ks);
+          else
+            return frag(base, wm + 32 * i + rr, ks);
+        };
+        auto fragB = [&](const uint16_t* base, int j, int ks) __attribute__((always_inline)) {
+          if constexpr (TB)
+            return fragT(base, wn + 32 * j, ks);
+          else
+            return frag(base, wn + 32 * j + rr, ks);
         };
         u32x4 ca[2][TM], cb[2][TN];
 #pragma unroll
@@ -572,7 +595,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
           if ((kRows >> i) & 1) ca[0][i] = fragA(rd, i, 0);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          if ((kCols >> j) & 1) cb[0][j] = frag(rd + kA, wn + 32 * j + rr, 0);
+          if ((kCols >> j) & 1) cb[0][j] = fragB(rd + kA, j, 0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int c = ks & 1;
@@ -582,7 +605,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
               if ((kRows >> i) & 1) ca[c ^ 1][i] = fragA(rd, i, ks + 1);
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-              if ((kCols >> j) & 1) cb[c ^ 1][j] = frag(rd + kA, wn + 32 * j + rr, ks + 1);
+              if ((kCols >> j) & 1) cb[c ^ 1][j] = fragB(rd + kA, j, ks + 1);
           }
 #pragma unroll
           for (int i = 0; i < TM; ++i)
@@ -596,18 +619,29 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
     int s = 0;
-    if constexpr (kAUpper) {  // the transposed stages come first; ntrans is a multiple of 4
-      for (; s + 2 <= ntrans; s += 2) {
-        step(std::true_type{}, b0, b1, s);
-        step(std::true_type{}, b1, b0, s + 1);
+    if constexpr (kUpper) {  // the transposed stages come first; ntA and ntB are multiples of 4
+      const int both = min(ntA, ntB);
+      for (; s + 2 <= both; s += 2) {
+        step(T_{}, T_{}, b0, b1, s);
+        step(T_{}, T_{}, b1, b0, s + 1);
+      }
+      for (; s + 2 <= ntA; s += 2) {
+        step(T_{}, F_{}, b0, b1, s);
+        step(T_{}, F_{}, b1, b0, s + 1);
+      }
+      for (; s + 2 <= ntB; s += 2) {
+        step(F_{}, T_{}, b0, b1, s);
+        step(F_{}, T_{}, b1, b0, s + 1);
       }
     }
     for (; s + 2 <= nstages; s += 2) {
-      step(std::false_type{}, b0, b1, s);
-      step(std::false_type{}, b1, b0, s + 1);
+      step(F_{}, F_{}, b0, b1, s);
+      step(F_{}, F_{}, b1, b0, s + 1);
     }
-    if (s < nstages) step(std::false_type{}, b0, b1, s);
+    if (s < nstages) step(F_{}, F_{}, b0, b1, s);
   };
   if constexpr (SYM && WAVES == 16) {
     switch (mask) {
@@ -656,7 +690,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
 
 template <class Epi>
 static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* bt, const typename Epi::Job* e,
-                              int njobs, int64_t n, int B, bool sym, int fmt, hipStream_t st, bool a_upper = false) {
+                              int njobs, int64_t n, int B, bool sym, int fmt, hipStream_t st, int upper = 0) {
   if (B % 128 != 0) return SHAMPOO_EUNSUPPORTED;
   if (!Epi::kSym && sym) return SHAMPOO_EINVAL;  // no symmetric epilogue
   const bool big = B % kBigTile == 0 && (sym ? Epi::kH16BigSym : Epi::kH16BigFull);
@@ -672,8 +706,9 @@ static inline int h16_gemm_nt(const uint16_t* const* a, const uint16_t* const* b
   P.B = B;
   P.tiles_n = B / T;
   P.tiles_per_item = sym ? P.tiles_n * (P.tiles_n + 1) / 2 : P.tiles_n * P.tiles_n;
-  if (a_upper && !(big && sym && has_a_upper<Epi>::value)) return SHAMPOO_EINVAL;  // only the large-tile kernel reads it
-  P.a_upper = a_upper ? 1 : 0;
+  // operands kept on and above the diagonal: only the large-tile kernel reads them
+  if (upper != 0 && (!(big && has_upper_operands<Epi>::value) || (upper >> (2 * njobs)) != 0)) return SHAMPOO_EINVAL;
+  P.upper = upper;
   const uint64_t total = (uint64_t)njobs * n * P.tiles_per_item;
   if (total == 0) return SHAMPOO_OK;
   if (total > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
@@ -752,7 +787,7 @@ static inline int bf16_gemm_nt_store(const uint16_t* a, const uint16_t* bt, cons
 // the rest of its row panels from those tiles, transposed.
 static inline int bf16_gemm_nt_clenshaw(const uint16_t* a, const uint16_t* bt, const EpiClenshaw::Job& e,
                                         int64_t n, int B, bool sym, bool a_upper, hipStream_t st) {
-  return h16_gemm_nt<EpiClenshaw>(&a, &bt, &e, 1, n, B, sym, H16_BF16, st, a_upper);
+  return h16_gemm_nt<EpiClenshaw>(&a, &bt, &e, 1, n, B, sym, H16_BF16, st, a_upper ? H16_UPPER_A : 0);
 }
 
 static inline int bf16_gemm_nt_bf16out(const uint16_t* a, const uint16_t* bt, uint16_t* out, int64_t n, int B,

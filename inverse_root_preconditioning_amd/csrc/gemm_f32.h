@@ -336,6 +336,19 @@ __device__ __forceinline__ void write4t_offdiag(Tile& t, int c, int r, const flo
   else
     t.write4t(c, r, o);
 }
+// Whether an off-diagonal tile writes anything at its mirrored place (a tile
+// without the `mirrored` query always does).
+template <class T, class = void>
+struct has_mirrored_query : std::false_type {};
+template <class T>
+struct has_mirrored_query<T, std::void_t<decltype(&T::mirrored)>> : std::true_type {};
+template <class Tile>
+__device__ __forceinline__ bool writes_mirror(const Tile& t) {
+  if constexpr (has_mirrored_query<Tile>::value)
+    return t.mirrored();
+  else
+    return true;
+}
 
 template <int TM, int TN, int KPRE, int SP = 0, class Tile>
 __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[TM][TN], int m0, int n0, int wm,
@@ -396,20 +409,22 @@ __device__ __forceinline__ void sym_epilogue_direct(Tile& tile, floatx16 (&acc)[
         const int c0 = n0 + wn + 32 * j, r0 = m0 + wm + 32 * i0;
         // on a diagonal tile: whether this lane's source block was computed by this wave
         const bool src = !decltype(DG)::value || ((mask >> ((i0 + cc / 32) * TN + j)) & 1);
+        if (decltype(DG)::value || writes_mirror(tile)) {
 #pragma unroll
-        for (int t = 0; t < 32 / RPI; ++t) {
-          const int tb = SP == 1 ? 4 * (t & 1) + 16 * (t >> 1) : RPI * t;  // >= 16 exactly for swizzled rows
-          const int row = tb + rrow;
-          const floatx4 v = *reinterpret_cast<const floatx4*>(stage + row * LDT + (tb >= 16 ? cc_sw : cc));
-          if constexpr (!decltype(DG)::value) {
-            write4t_offdiag(tile, c0 + row, r0 + cc, v);
-          } else if (src) {
-            if (r0 + cc + 3 < c0 + row) {
-              tile.write4t(c0 + row, r0 + cc, v);
-            } else {
+          for (int t = 0; t < 32 / RPI; ++t) {
+            const int tb = SP == 1 ? 4 * (t & 1) + 16 * (t >> 1) : RPI * t;  // >= 16 exactly for swizzled rows
+            const int row = tb + rrow;
+            const floatx4 v = *reinterpret_cast<const floatx4*>(stage + row * LDT + (tb >= 16 ? cc_sw : cc));
+            if constexpr (!decltype(DG)::value) {
+              write4t_offdiag(tile, c0 + row, r0 + cc, v);
+            } else if (src) {
+              if (r0 + cc + 3 < c0 + row) {
+                tile.write4t(c0 + row, r0 + cc, v);
+              } else {
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (r0 + cc + e < c0 + row) tile.write(c0 + row, r0 + cc + e, v[e]);
+                for (int e = 0; e < 4; ++e)
+                  if (r0 + cc + e < c0 + row) tile.write(c0 + row, r0 + cc + e, v[e]);
+              }
             }
           }
         }
@@ -996,6 +1011,7 @@ struct EpiStore {
   static constexpr bool kBigStaged = false;  // full products of the large kernel: register-direct epilogue
   static constexpr bool kH16BigSym = true, kH16BigFull = false;
   static constexpr int kH16BigWaves = 16;
+  static constexpr bool kH16Upper = true;  // operands and 16-bit copy may be kept on and above the diagonal only
   struct Job {
     float* out;          // fp32 output (may be null when only the 16-bit copy is needed)
     const float* cin;
@@ -1005,12 +1021,17 @@ struct EpiStore {
     float pexp, extra;
     uint16_t* out16;     // optional 16-bit copy of the output (operand of a later product)
     int fmt16;           // H16_BF16 or H16_F16
+    // symmetric products on the large 16-bit kernel: the 16-bit copy only in
+    // tiles on and above the diagonal (the mirrored half is not written; the
+    // other kernels write it in full)
+    int upper16;
   };
   struct Tile {
     static constexpr int kPrefetch = 0;
     float* out;
     const float* cin;
     uint16_t* o16;
+    uint16_t* o16m;      // the 16-bit copy's mirrored half of an off-diagonal tile (null: not written)
     int fmt;
     float mult, beta;
     bool ident;
@@ -1020,6 +1041,7 @@ struct EpiStore {
       out = j.out ? j.out + off : nullptr;
       cin = j.cin ? j.cin + off : nullptr;
       o16 = j.out16 ? j.out16 + off : nullptr;
+      o16m = j.upper16 ? nullptr : o16;
       fmt = j.fmt16;
       beta = j.beta;
       mult = j.alpha;
@@ -1048,6 +1070,13 @@ struct EpiStore {
       if (out) stg(reinterpret_cast<floatx4*>(out + idx), o);
       if (o16) stg4_h16(o16 + idx, o, fmt);
     }
+    // the mirrored entries of an off-diagonal tile
+    __device__ __forceinline__ void write4t_mirror(int c, int r, const floatx4& o) {
+      const int64_t idx = (int64_t)c * B + r;
+      if (out) stg(reinterpret_cast<floatx4*>(out + idx), o);
+      if (o16m) stg4_h16(o16m + idx, o, fmt);
+    }
+    __device__ __forceinline__ bool mirrored() const { return out != nullptr || o16m != nullptr; }
     __device__ __forceinline__ void write_upper(int row, int col, float o) { write(row, col, o); }
     // row `row`, columns col..col+3 (col..col+7), on or above the diagonal
     __device__ __forceinline__ void write_upper4(int row, int col, const floatx4& o) { write4t(row, col, o); }
@@ -1156,6 +1185,7 @@ struct EpiCnM {
   // 16-bit: the 8-wave layout with its epilogue through LDS
   static constexpr bool kH16BigSym = true, kH16BigFull = true;
   static constexpr int kH16BigWaves = 8;
+  static constexpr bool kH16Upper = true;  // operands may be kept on and above the diagonal only
   static constexpr bool kReduce = true;
   struct Job {
     float* m;            // fp32 outputs (null: not written)
@@ -1240,7 +1270,7 @@ struct EpiCnM {
 //   X = mult (cj I + 2 acc - b1 - b2), I if degenerate   (final == 1, cj = c_0)
 // An optional 16-bit copy of b is written for the next half-width product.
 struct EpiClenshaw {
-  static constexpr bool kH16AUpper = true;  // may keep its 16-bit copy on and above the diagonal only
+  static constexpr bool kH16Upper = true;  // operands and 16-bit copy may be kept on and above the diagonal only
   static constexpr bool kReduce = false;
   static constexpr bool kSym = true;
   static constexpr bool kDirect = true;

@@ -424,6 +424,7 @@ EpiStore::Job final_job(const FinalOut& fo) {
   j.status = fo.status;
   j.pexp = fo.pexp;
   j.extra = fo.extra;
+  j.upper16 = 0;
   return j;
 }
 
@@ -439,6 +440,7 @@ EpiStore::Job plain_job(float* out, uint16_t* out16 = nullptr, int fmt16 = H16_B
   j.status = nullptr;
   j.pexp = 0.f;
   j.extra = 1.f;
+  j.upper16 = 0;
   return j;
 }
 
@@ -739,6 +741,9 @@ int coupled_newton(const float* F, const shampoo_scale* sc, int64_t nf, int B, i
 // is in NT form with the row-major fp16 copy of the right operand standing
 // for its transpose: C, C^2, C^4 and M are polynomials in A_s, symmetric in
 // exact arithmetic, and their rounding asymmetry is far below fp16 precision.
+// With B a multiple of 256 the symmetric products (X C, C^2, C^4) keep their
+// fp16 result only in the tiles on and above the diagonal, and the products
+// that take it read the rest of each panel from there, transposed.
 // ---------------------------------------------------------------------------
 int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p, int iters, float* x,
                        float* resid, int32_t* status, Cn16Ws* ws, hipStream_t st, bool sym, bool sym_c) {
@@ -790,17 +795,27 @@ int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int 
     SHP_TRY(run_resid(ws->partials, a.chunks, resid, iters, 0, ws->rmin, true, status, nf, st));
   }
   const int tiles = (B / h16_tile_of(B, sym_c)) * (B / h16_tile_of(B, sym_c));  // reduction partials of C^p M
+  // symmetric products write their fp16 result on and above the diagonal only
+  // (the large-tile kernel, which the products reading it also take)
+  const int up = (sym && B % kBigTile == 0) ? 1 : 0;
+  auto upper_job = [up](uint16_t* out16) {
+    EpiStore::Job j = plain_job(nullptr, out16, H16_F16);
+    j.upper16 = up;
+    return j;
+  };
   uint16_t* X = nullptr;
+  bool x_up = false;  // X holds only its upper tiles
   for (int it = 0; it < iters; ++it) {
     if (it == iters - 1) {
       FinalOut fo{x, sc, status, pexp, 1.f};
       EpiStore::Job j = final_job(fo);
       const uint16_t* A[1] = {X};
       const uint16_t* Bt[1] = {C};
-      return h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st);
+      return h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st, x_up ? H16_UPPER_A : 0);
     }
     if (it == 0) X = C;  // X_1 = C_0; the buffer now belongs to X
     uint16_t* Cp = C;
+    bool cp_up = false;
     uint16_t* Xn = nullptr;
     if (p >= 2) {
       uint16_t* C2 = pool.get();
@@ -808,34 +823,36 @@ int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int 
       if (it > 0) {
         Xn = pool.get();
         if (Xn == nullptr) return SHAMPOO_EWORKSPACE;
-        EpiStore::Job j[2] = {plain_job(nullptr, Xn, H16_F16), plain_job(nullptr, C2, H16_F16)};
+        EpiStore::Job j[2] = {upper_job(Xn), upper_job(C2)};
         const uint16_t* A[2] = {X, C};
         const uint16_t* Bt[2] = {C, C};
-        SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, j, 2, nf, B, sym, H16_F16, st));
+        SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, j, 2, nf, B, sym, H16_F16, st, x_up ? H16_UPPER_A : 0));
       } else {
-        EpiStore::Job j = plain_job(nullptr, C2, H16_F16);
+        EpiStore::Job j = upper_job(C2);
         const uint16_t* A[1] = {C};
         const uint16_t* Bt[1] = {C};
         SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st));
       }
       Cp = C2;
+      cp_up = up;
       for (int q = 4; q <= p; q *= 2) {
         uint16_t* Cq = pool.get();
         if (Cq == nullptr) return SHAMPOO_EWORKSPACE;
-        EpiStore::Job j = plain_job(nullptr, Cq, H16_F16);
+        EpiStore::Job j = upper_job(Cq);
         const uint16_t* A[1] = {Cp};
         const uint16_t* Bt[1] = {Cp};
-        SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st));
+        SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st,
+                                      cp_up ? (H16_UPPER_A | H16_UPPER_B) : 0));
         pool.put(Cp);
         Cp = Cq;
       }
     } else if (it > 0) {
       Xn = pool.get();
       if (Xn == nullptr) return SHAMPOO_EWORKSPACE;
-      EpiStore::Job j = plain_job(nullptr, Xn, H16_F16);
+      EpiStore::Job j = upper_job(Xn);
       const uint16_t* A[1] = {X};
       const uint16_t* Bt[1] = {C};
-      SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st));
+      SHP_TRY(h16_gemm_nt<EpiStore>(A, Bt, &j, 1, nf, B, sym, H16_F16, st, x_up ? H16_UPPER_A : 0));
     }
     uint16_t* Mn = pool.get();
     uint16_t* Cn = pool.get();
@@ -853,7 +870,7 @@ int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int 
       const uint16_t* A[1] = {Cp};
       const uint16_t* Bt[1] = {M};
       timing_before(SHAMPOO_TIME_CN_M, st);
-      const int rc = h16_gemm_nt<EpiCnM>(A, Bt, &j, 1, nf, B, sym_c, H16_F16, st);
+      const int rc = h16_gemm_nt<EpiCnM>(A, Bt, &j, 1, nf, B, sym_c, H16_F16, st, cp_up ? H16_UPPER_A : 0);
       timing_after(SHAMPOO_TIME_CN_M, st);
       SHP_TRY(rc);
       SHP_TRY(run_resid(ws->partials, tiles, resid, iters, it + 1, ws->rmin, false, status, nf, st));
@@ -864,6 +881,7 @@ int coupled_newton_h16(const float* F, const shampoo_scale* sc, int64_t nf, int 
       pool.put(X);
       pool.put(C);
       X = Xn;
+      x_up = up;
     }
     M = Mn;
     C = Cn;
@@ -1060,6 +1078,7 @@ int shampoo_accumulate(const shampoo_block* g_blocks, int64_t nblocks, int B, fl
   jl.status = nullptr;
   jl.pexp = 0.f;
   jl.extra = 1.f;
+  jl.upper16 = 0;
   EpiStore::Job jr = jl;
   jr.out = factors + stack_elems(nblocks, B);
   jr.cin = jr.out;

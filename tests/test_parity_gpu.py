@@ -507,6 +507,35 @@ def test_coupled_newton_fp16_matches_oracle(B, p, iters, full):
     report("cn_fp16", B=B, p=p, iters=iters, full=full, err=err)
 
 
+@pytest.mark.parametrize("sym_c", [False, True])
+@pytest.mark.parametrize("B", [512, 768])
+@pytest.mark.parametrize("p,iters", [(1, 5), (2, 5), (4, 5), (8, 4)])
+def test_coupled_newton_fp16_upper_operands(B, p, iters, sym_c):
+    """With B a multiple of 256, fp16 coupled Newton keeps the fp16 results of
+    its symmetric products (X C, C^2, C^4, ...) on and above the diagonal only,
+    and the next products read the lower tiles of their panels transposed from
+    there: as the left operand (X C, C^p M, the final X C), as both operands
+    (C^2 C^2), in symmetric and full C^p M products.  2 x 2 and 3 x 3 tiles
+    per factor, each p, against the float64 coupled Newton."""
+    nf = 2
+    F = W.spd_factors(170 + B + p, nf, B, cond=1e3)
+    V0 = W.start_vectors(171, nf, B)
+    Fd = dev(F)
+    sc, st = gpu_scale(Fd, 0.0, capi.SCALE_POWER, dev(V0))
+    v = capi.CN_F16 | (capi.SYM_COUPLING if sym_c else 0)
+    X, R = gpu_roots(Fd, sc, st, "newton", iters=iters, p=p, variant=v, resid=True)
+    Xh, Rh = host(X), host(R)
+    err = 0.0
+    for i in range(nf):
+        o = oracle_scale(F[i], 0.0, capi.SCALE_POWER, V0[i])
+        err = max(err, O.relative_frobenius(Xh[i], oracle_root(F[i], o, "newton", iters=iters, p=p,
+                                                                variant=capi.CN)))
+        assert np.array_equal(Xh[i], Xh[i].T)
+    assert err <= TOL_BF16, err
+    assert np.all(np.isfinite(Rh)) and np.all(Rh >= 0.0)
+    report("cn_fp16_upper", B=B, p=p, iters=iters, sym_c=sym_c, err=err)
+
+
 @pytest.mark.parametrize("B", [384, 512, 1280])
 def test_half_width_products_span_tiles(B):
     """The 16-bit products on several tiles per factor: B = 384 runs the
