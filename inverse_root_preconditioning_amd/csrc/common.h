@@ -109,13 +109,13 @@ __device__ __forceinline__ uint16_t to_h16(float x, int fmt) {
 }
 
 // Two 16-bit values of format fmt (a in the low half) in one dword, each
-// rounded to nearest even.
+// rounded to nearest even.  Both conversions and a select: a branch on the
+// (uniform) format per pair costs more in the store loops of the epilogues.
 __device__ __forceinline__ uint32_t pack_h16x2(float a, float b, int fmt) {
-  if (fmt == H16_F16) {
-    const f32x2_t v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
-  }
-  return pack_bf16x2(a, b);
+  const f32x2_t v = {a, b};
+  const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+  const uint32_t g = pack_bf16x2(a, b);
+  return fmt == H16_F16 ? h : g;
 }
 
 // Four consecutive 16-bit copies of o at p (p 8-byte aligned).
