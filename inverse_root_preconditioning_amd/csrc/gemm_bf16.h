@@ -436,12 +436,18 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
   constexpr int kA = BM * BKS, kStage = (BM + BN) * BKS;  // 16-bit elements
   constexpr int LA = BM * CPR / NT;                      // chunks of A (and of Bt) per thread and stage
   constexpr int KS = BKS / 16;
-  constexpr int PH = 4;                                  // phases of the symmetric epilogue's transpose
-  constexpr int kFloats = 2 * kStage / 2;                // the stage buffers, counted in floats
+  // Phases of the LDS-staged epilogue (8 waves): two of 128 rows, four waves
+  // staging at a time (C^p M of fp16 coupled Newton 1.70 -> 1.65 ms per launch
+  // against four phases of 64 rows), which takes 130 KB of LDS beside the
+  // 128 KB of stage buffers; the 16-wave register epilogues stage per wave.
+  constexpr int PH = WAVES == 8 ? 2 : 4;
+  constexpr int kStageFloats = 2 * kStage / 2;           // the stage buffers, counted in floats
+  constexpr int kStaged = (BM / PH) * (BN + 4) + NT / kWave;  // one phase's rows and the reduction slots
+  constexpr int kFloats = kStaged > kStageFloats ? kStaged : kStageFloats;
   static_assert(LA * NT == BM * CPR && BN == BM, "chunking");
-  static_assert((BM / PH) * (BN + 4) + NT / kWave <= kFloats, "staging and reduction fit the buffers");
+  static_assert(kFloats * 4 <= 160 * 1024, "fits the LDS");
   // One LDS object only (see gemm_f32_big_kernel).
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kFloats];
   float* const red = reinterpret_cast<float*>(lds) + kFloats - NT / kWave;
 
   int job, tm, tn;
