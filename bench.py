@@ -238,7 +238,13 @@ def family_info(fam, wl, B, nf, capi):
       Clenshaw, bf16 input:  read the bf16 A_s^T and b1 copies, b1 and b2
                              (fp32) at the upper entries, write b (fp32)
                              at the upper entries and its bf16 copy    12 B^2
-      coupled Newton C^p M:  read C^p, M, write M, C: fp32 16 B^2, fp16 8 B^2"""
+                             (10 B^2 with B a multiple of 256, where the
+                             bf16 b1 and b copies are kept on and above
+                             the diagonal, counted as a triangle: B^2 each)
+      coupled Newton C^p M:  read C^p, M, write M, C: fp32 16 B^2, fp16 8 B^2
+                             (fp16 with B a multiple of 256 and symmetric
+                             products: C^p kept on and above the diagonal,
+                             read as a triangle, 7 B^2)"""
     sym = float(B) * B * (B + 1)   # one symmetric product: upper triangle with the diagonal
     full = 2.0 * B ** 3
     b2 = float(B) * B
@@ -260,16 +266,20 @@ def family_info(fam, wl, B, nf, capi):
             k = "gemm_h16_big_kernel<EpiClenshaw, bf16, 8 waves>" if big else "gemm_h16_nt_kernel<EpiClenshaw, bf16>"
         else:
             k = f32k + "<EpiClenshaw>"
+        upper16 = bf and big and not full_all
         return (k + " (one symmetric Clenshaw product per factor, upper tiles)", nf * (full if full_all else sym),
-                nf * (12 if bf else 16) * b2, PEAK_BF16_MFMA if bf else PEAK_F32_MFMA)
+                nf * ((10 if upper16 else 12) if bf else 16) * b2, PEAK_BF16_MFMA if bf else PEAK_F32_MFMA)
     half = (v & 0xff) == capi.CN_F16
     if half:
         k = "gemm_h16_big_kernel<EpiCnM, fp16, 8 waves>" if big else "gemm_h16_nt_kernel<EpiCnM, fp16>"
     else:
         k = f32k + "<EpiCnM>"
+    p = wl.get("p", 4)
+    upper16 = half and big and not full_all and p >= 2  # p = 1: C^p is C, kept in full
     return (k + " (coupled Newton C^p M with C = ((p+1)I - M)/p and the residual, "
             + ("upper tiles" if sym_c else "full product") + ")",
-            nf * (sym if sym_c else full), nf * (8 if half else 16) * b2, PEAK_BF16_MFMA if half else PEAK_F32_MFMA)
+            nf * (sym if sym_c else full), nf * ((7 if upper16 else 8) if half else 16) * b2,
+            PEAK_BF16_MFMA if half else PEAK_F32_MFMA)
 
 
 FAMILY_KEYS = {1: "ndb_pair", 2: "ndb_p", 4: "clenshaw", 8: "cn_m"}
