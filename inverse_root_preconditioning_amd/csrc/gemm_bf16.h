@@ -602,6 +602,11 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           if ((kCols >> j) & 1) cb[0][j] = fragB(rd + kA, j, 0);
+        // LDS reads per k-step (a transposed fragment takes two) and MFMAs per k-step
+        constexpr int kReads = (TA ? 2 : 1) * __builtin_popcount(kRows) + (TB ? 2 : 1) * __builtin_popcount(kCols);
+        constexpr int kMfma = __builtin_popcount(kMask);
+        constexpr int kPairs = kReads < kMfma ? kReads : kMfma;
+        __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int c = ks & 1;
@@ -618,6 +623,21 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
 #pragma unroll
             for (int j = 0; j < TN; ++j)
               if ((kMask >> (i * TN + j)) & 1) acc[i][j] = mfma_h16<FMT>(ca[c][i], cb[c][j], acc[i][j]);
+          // Interleave the next k-step's fragment reads with this k-step's
+          // MFMAs (one MFMA, one LDS read), so that their latency runs under
+          // the matrix core instead of ahead of it; left to itself the
+          // scheduler issued all reads, waited for them, then the MFMAs.
+          if (ks + 1 < KS) {
+#pragma unroll
+            for (int q = 0; q < kPairs; ++q) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            if constexpr (kMfma > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPairs, 0);
+            if constexpr (kReads > kPairs) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kPairs, 0);
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+          }
         }
       }
       __builtin_amdgcn_s_waitcnt(kWaitAll);
