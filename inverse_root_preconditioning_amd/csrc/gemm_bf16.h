@@ -482,20 +482,21 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
   const int rr = lane & 31, h = lane >> 5;
 
   constexpr bool kUpper = has_upper_operands<Epi>::value;
-  const uint16_t* srcA[LA];
-  const uint16_t* srcB[LA];
-  const uint16_t* srcAT[kUpper ? LA : 1];
-  const uint16_t* srcBT[kUpper ? LA : 1];
+  // Element offsets of this thread's 16-byte chunks from the item's base, for
+  // plain stages and (kUpper) transposed ones; 32 bits hold them (B <= 16384,
+  // so B * B < 2^31).  A stage picks its base as a uniform value and each
+  // chunk's offset with a select, so that the load addresses carry no branch.
+  uint32_t offA[LA], offB[LA], offAT[kUpper ? LA : 1], offBT[kUpper ? LA : 1];
 #pragma unroll
   for (int it = 0; it < LA; ++it) {
     const int c = it * NT + tid, row = c / CPR, cs = (c % CPR) ^ h16_swz(c / CPR);
-    srcA[it] = A + (int64_t)(m0 + row) * B + 8 * cs;
-    srcB[it] = Bt + (int64_t)(n0 + row) * B + 8 * cs;
+    offA[it] = (uint32_t)(m0 + row) * (uint32_t)B + 8 * cs;
+    offB[it] = (uint32_t)(n0 + row) * (uint32_t)B + 8 * cs;
     if constexpr (kUpper) {
       // transposed stage: row kr of the 64 k-rows, 16-byte chunk cc of its 256 columns (h16_tswz)
       const int kr = c / (BM / 8), cc = c % (BM / 8);
-      srcAT[it] = A + (int64_t)kr * B + m0 + 8 * (cc ^ h16_tswz(kr));
-      srcBT[it] = Bt + (int64_t)kr * B + n0 + 8 * (cc ^ h16_tswz(kr));
+      offAT[it] = (uint32_t)kr * (uint32_t)B + m0 + 8 * (cc ^ h16_tswz(kr));
+      offBT[it] = (uint32_t)kr * (uint32_t)B + n0 + 8 * (cc ^ h16_tswz(kr));
     }
   }
   const int nstages = B / BKS;
@@ -506,18 +507,24 @@ __global__ void __launch_bounds__(64 * WAVES, 1) gemm_h16_big_kernel(const H16La
   const int ntB = (up & H16_UPPER_B) ? min(n0 / BKS, nstages) : 0;
   auto issue = [&](uint16_t* __restrict__ buf, int s) __attribute__((always_inline)) {
     const int k0 = min(s, nstages - 1) * BKS;
+    const bool tA = kUpper && s < ntA, tB = kUpper && s < ntB;
+    // k-columns k0.. of the plain panel, or k-rows k0.. of the transposed one
+    const uint16_t* const baseA = A + (tA ? (int64_t)k0 * B : (int64_t)k0);
+    const uint16_t* const baseB = Bt + (tB ? (int64_t)k0 * B : (int64_t)k0);
+    // the offsets picked by uniform masks on their values (a plain select let
+    // the compiler pick between the two arrays in memory instead)
+    const uint32_t mA = tA ? ~0u : 0u, mB = tB ? ~0u : 0u;
 #pragma unroll
     for (int it = 0; it < LA; ++it) {
-      const uint16_t* pa = srcA[it] + k0;
-      const uint16_t* pb = srcB[it] + k0;
+      uint32_t oa = offA[it], ob = offB[it];
       if constexpr (kUpper) {
-        if (s < ntA) pa = srcAT[it] + (int64_t)k0 * B;
-        if (s < ntB) pb = srcBT[it] + (int64_t)k0 * B;
+        oa = (offAT[it] & mA) | (oa & ~mA);
+        ob = (offBT[it] & mB) | (ob & ~mB);
       }
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pa,
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(baseA + oa),
                                        (__attribute__((address_space(3))) void*)(buf + (it * NT + wave * 64) * 8),
                                        16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)pb,
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(baseB + ob),
                                        (__attribute__((address_space(3))) void*)(buf + kA + (it * NT + wave * 64) * 8),
                                        16, 0, 0);
     }
