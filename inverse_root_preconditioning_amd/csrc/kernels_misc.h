@@ -687,7 +687,11 @@ __global__ void __launch_bounds__(256) ew_kernel(const EwArgs P) {
 // EW_CHEBY_START forms it, written in fp32, together with the bf16 copy of
 // b_{d-1} and the transposed bf16 copy of A_s (the NT operand of the Clenshaw
 // products); A_s itself is not stored, nor b_d = c_d I unless `bd` is given
-// (the first Clenshaw step forms it).  B is a multiple of 64.
+// (the first Clenshaw step forms it).  B is a multiple of 64.  With `split`
+// (the large-tile Clenshaw products, B a multiple of 256) only what they read
+// is written: fp32 b_{d-1} in the 256 x 256 tiles on and below the diagonal
+// (their epilogues read it at transposed positions of upper entries), its
+// bf16 copy in those on and above it (an upper-only operand).
 struct Cheby16StartArgs {
   const float* x;            // factors [nf][B][B]
   const shampoo_scale* sc;   // c and eps per factor
@@ -699,6 +703,7 @@ struct Cheby16StartArgs {
   float cd, cd1;             // c_d, c_{d-1}
   int B;
   int tiles;                 // (B / 64)^2
+  int split;                 // write fp32 b_{d-1} below, its bf16 copy above the diagonal (256 x 256 tiles)
 };
 
 __global__ void __launch_bounds__(256) cheby16_start_kernel(const Cheby16StartArgs P) {
@@ -716,6 +721,9 @@ __global__ void __launch_bounds__(256) cheby16_start_kernel(const Cheby16StartAr
   const int64_t base = f * (int64_t)P.B * P.B;
   const int tid = threadIdx.x;
   const int cr = tid >> 4, cc = (tid & 15) * 4;
+  // this 64 x 64 tile lies in one 256 x 256 tile (tr, tc)
+  const int tr = r0 / 256, tc = c0 / 256;
+  const bool w32 = !P.split || tr >= tc, w16 = !P.split || tr <= tc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = r0 + cr + 16 * i, col = c0 + cc;
@@ -731,8 +739,8 @@ __global__ void __launch_bounds__(256) cheby16_start_kernel(const Cheby16StartAr
       t[cr + 16 * i][cc + e] = y;
     }
     if (P.bd) stg(reinterpret_cast<floatx4*>(P.bd + idx), o1);
-    stg(reinterpret_cast<floatx4*>(P.bd1 + idx), o2);
-    stg4_h16(P.bd1_16 + idx, o2, H16_BF16);
+    if (w32) stg(reinterpret_cast<floatx4*>(P.bd1 + idx), o2);
+    if (w16) stg4_h16(P.bd1_16 + idx, o2, H16_BF16);
   }
   __syncthreads();
 #pragma unroll

@@ -933,6 +933,9 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
   const bool bf = (prec == SHAMPOO_BF16_IN);
   int i2 = 0, i1 = 1, i0 = 2;  // ring slots of b_{j+2}, b_{j+1}, b_j
   int s1 = 0;                  // bf16 slot holding b_{j+1}
+  // bf16 terms on the large-tile kernel keep their 16-bit copy only in the tiles
+  // on and above the diagonal; the next product reads the rest transposed
+  const bool up = bf && sym && (B % kBigTile) == 0;
   if (bf) {
     // b_{d-1} and the 16-bit operands in one pass: A_s is needed only as bf16,
     // and b_d = c_d I is formed by the first Clenshaw step
@@ -948,6 +951,7 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
     s.cd1 = (float)c[degree - 1];
     s.B = B;
     s.tiles = (B / 64) * (B / 64);
+    s.split = up ? 1 : 0;
     const uint64_t grid = (uint64_t)nf * s.tiles;
     if (grid > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
     if (grid > 0) hipLaunchKernelGGL(cheby16_start_kernel, dim3((uint32_t)grid), dim3(256), 0, st, s);
@@ -960,9 +964,6 @@ int chebyshev(const float* F, const shampoo_scale* sc, int64_t nf, int B, int p,
     a.c1 = (float)c[degree - 1];
     SHP_TRY(run_ew<EW_CHEBY_START>(a, nf, st));
   }
-  // bf16 terms on the large-tile kernel keep their 16-bit copy only in the tiles
-  // on and above the diagonal; the next product reads the rest transposed
-  const bool up = bf && sym && (B % kBigTile) == 0;
   for (int j = degree - 2; j >= 0; --j) {
     EpiClenshaw::Job e;
     e.upper16 = up ? 1 : 0;
