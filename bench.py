@@ -285,6 +285,41 @@ def family_info(fam, wl, B, nf, capi):
 FAMILY_KEYS = {1: "ndb_pair", 2: "ndb_p", 4: "clenshaw", 8: "cn_m"}
 
 
+def stage_rates(wl, cfg, B, n, nf, stages, capi):
+    """Algorithmic rates of the stages around the roots, from the stage-split
+    step (HIP events between the stages on the step's stream), each against
+    the lower roofline at its arithmetic intensity:
+      accumulate:   two symmetric products per block, B^2 (B + 1) flops each;
+                    20 B^2 bytes per block (G read, L and R read and written)
+      scale:        power iteration, T + 1 products F V of r columns per
+                    factor: 2 B^2 r (T + 1) flops and 4 B^2 (T + 1) bytes (F
+                    read each round; fp32 MFMA); Frobenius: F read once
+      precondition: two full products per block, 4 B^3 flops; 16 B^2 bytes
+                    per block (X_L, X_R and G read, U written)
+    The products run on bf16-input MFMA for bf16-input workloads, else fp32."""
+    b2 = float(B) * B
+    mm = PEAK_BF16_MFMA if wl["prec"] == capi.BF16_IN else PEAK_F32_MFMA
+    if cfg.scale_mode == capi.SCALE_POWER:
+        t1 = cfg.pi_steps + 1
+        sc = (nf * 2 * b2 * cfg.pi_starts * t1, nf * 4 * b2 * t1, PEAK_F32_MFMA)
+    else:
+        sc = (nf * 2 * b2, nf * 4 * b2, PEAK_F32_MFMA)
+    work = {"accumulate": (n * 2 * b2 * (B + 1), n * 20 * b2, mm), "scale": sc,
+            "precondition": (n * 4.0 * B ** 3, n * 16 * b2, mm)}
+    out = {}
+    for name, (flops, nbytes, peak) in work.items():
+        ms = stages.get(name)
+        if not ms:
+            continue
+        tflops, gbs = flops / (ms * 1e-3) / 1e12, nbytes / (ms * 1e-3) / 1e9
+        hbm = flops / nbytes < peak * 1e12 / (PEAK_HBM * 1e9)
+        out[name] = {"ms": round(ms, 3), "tflops": round(tflops, 2), "gbs": round(gbs, 1),
+                     "bound": "hbm" if hbm else "mfma", "peak": PEAK_HBM if hbm else peak,
+                     "frac": round(gbs / PEAK_HBM if hbm else tflops / peak, 4),
+                     "flops": flops, "bytes": nbytes}
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -550,6 +585,7 @@ def main(argv=None):
         "roofline": roofline,
         "kernels": kernels,
         "stages_ms": {k: round(v, 3) for k, v in stages.items()},
+        "stage_rates": stage_rates(wl, cfg, B, n, nf, stages, capi),
         "invroot_blocks_per_s": round(nf / (stages["invroot"] * 1e-3), 2),
         "status_nonzero_factors": int((status != 0).sum()),
     }
