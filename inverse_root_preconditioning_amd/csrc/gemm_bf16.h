@@ -810,9 +810,62 @@ static inline int bf16_gemm_nt(const uint16_t* a, const uint16_t* bt, const type
   return h16_gemm_nt<Epi>(&a, &bt, &e, 1, n, B, sym, H16_BF16, st);
 }
 
+// The bf16 EMA Gram products (L <- beta L + alpha G G^T in place) on the
+// large tiles: the 8-wave layout, whose registers let the epilogue request the
+// old factor 4 groups ahead.  It reads the old factor at the entry's own
+// position (4 rows of one column per group): the product is updated in place
+// and the mirrored writes of a tile land on its transposed positions.
+struct EpiStoreEma : EpiStore {
+  static constexpr int kH16BigWaves = 8;
+  struct Tile : EpiStore::Tile {
+    static constexpr int kPrefetch = 4;
+    struct Pre {
+      floatx4 x;
+    };
+    __device__ __forceinline__ Tile(const Job& j, int64_t item, int B_) : EpiStore::Tile(j, item, B_) {}
+    __device__ __forceinline__ Pre prefetch4(int r, int c) const {
+      Pre p;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p.x[e] = ldg(cin + (int64_t)(r + e) * B + c);
+      return p;
+    }
+    __device__ __forceinline__ floatx4 value4p(int r, int c, const floatx4& v, const Pre& p) const {
+      floatx4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = mult * v[e];
+        x += beta * p.x[e];
+        o[e] = ident ? ((r + e == c) ? 1.f : 0.f) : x;
+      }
+      return o;
+    }
+    __device__ __forceinline__ floatx4 value4(int r, int c, const floatx4& v) const {
+      return value4p(r, c, v, prefetch4(r, c));
+    }
+  };
+};
+
 static inline int bf16_gemm_nt_store(const uint16_t* a, const uint16_t* bt, const EpiStore::Job& e, int64_t n,
                                      int B, bool sym, hipStream_t st) {
-  return bf16_gemm_nt<EpiStore>(a, bt, e, n, B, sym, st);
+  if (!(sym && B % kBigTile == 0 && e.cin != nullptr && e.out != nullptr && e.out16 == nullptr &&
+        e.scale == nullptr && e.status == nullptr))
+    return bf16_gemm_nt<EpiStore>(a, bt, e, n, B, sym, st);
+  H16Launch<EpiStoreEma> P;
+  memset(&P, 0, sizeof(P));
+  P.a[0] = a;
+  P.bt[0] = bt;
+  P.e[0] = e;
+  P.nitems = n;
+  P.B = B;
+  P.tiles_n = B / kBigTile;
+  P.tiles_per_item = P.tiles_n * (P.tiles_n + 1) / 2;
+  const uint64_t total = (uint64_t)n * P.tiles_per_item;
+  if (total == 0) return SHAMPOO_OK;
+  if (total > 0x7fffffffull) return SHAMPOO_EUNSUPPORTED;
+  P.total = (uint32_t)total;
+  constexpr int W = EpiStoreEma::kH16BigWaves;
+  hipLaunchKernelGGL((gemm_h16_big_kernel<EpiStoreEma, H16_BF16, true, W>), dim3(P.total), dim3(64 * W), 0, st, P);
+  return hipGetLastError() == hipSuccess ? SHAMPOO_OK : SHAMPOO_EHIP;
 }
 
 // a_upper: `a` (the previous Clenshaw term) holds only its tiles on and above

@@ -537,6 +537,33 @@ def test_coupled_newton_fp16_upper_operands(B, p, iters, sym_c):
 
 
 @pytest.mark.parametrize("B", [384, 512, 1280])
+def test_accumulate_bf16_ema_over_prior_state(B):
+    """bf16-input EMA steps over a nonzero state, two in a row, each checked
+    against the oracle's step from the GPU's previous state: the old factor
+    enters through the epilogue's loads (on the 256 x 256 tiles requested
+    groups ahead, at each entry's own position, with the factor updated in
+    place).  The prior is a Gram matrix of the product's own size with weight
+    0.9, so an entry read from the wrong place would be an O(1) error; the
+    state must stay exactly symmetric."""
+    n = 2
+    G0, G1, G2 = (grads(170 + B + t, n, B, 0.02) for t in range(3))
+    prior = np.stack([m for i in range(n) for m in O.accumulate(np.zeros((B, B)), np.zeros((B, B)), G0[i], 0.0, 1.0)])
+    prior = np.concatenate([prior[0::2], prior[1::2]]).astype(np.float32)  # all L, then all R
+    F = dev(prior)
+    for t, G in enumerate((G1, G2)):
+        prev = host(F).astype(np.float64)
+        PL.accumulate(PL.BlockTable.from_stack(dev(G)), F, 0.9, 0.1, prec=capi.BF16_IN)
+        out = host(F)
+        err = 0.0
+        for i in range(n):
+            L, R = O.accumulate(prev[i], prev[n + i], G[i], 0.9, 0.1)
+            err = max(err, O.relative_frobenius(out[i], L), O.relative_frobenius(out[n + i], R))
+            assert np.array_equal(out[i], out[i].T) and np.array_equal(out[n + i], out[n + i].T)
+        assert err <= TOL_BF16, (t, err)
+        report("accumulate_bf16_ema", B=B, step=t, err=err)
+
+
+@pytest.mark.parametrize("B", [384, 512, 1280])
 def test_half_width_products_span_tiles(B):
     """The 16-bit products on several tiles per factor: B = 384 runs the
     128 x 128 workgroup tile (3 x 3 tiles), B = 512 and 1280 the 256 x 256 ones
